@@ -1,0 +1,159 @@
+"""Exact IO-aware attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of the C ABI in include/fa.h (libfa355.so).  Every step of the
+computation runs in the library's HIP kernels; this module only marshals torch tensors
+(device memory and the current stream) into the C calls.  There is no fallback path:
+if the library is missing or a call fails, an exception is raised.
+
+Low-level calls with the C names (caller allocates every output):
+    fa_forward(q, k, v, o, lse, scale, causal, kv_len=None, stream=None)
+    fa_backward(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
+                kv_len=None, stream=None)
+    fa_backward_workspace_size(B, H, N, d)
+
+Convenience wrappers that allocate outputs with torch:
+    forward(q, k, v, causal=False, scale=None, kv_len=None) -> (o, lse)
+    backward(q, k, v, o, dout, lse, causal=False, scale=None, kv_len=None) -> (dq, dk, dv)
+
+Tensors: q, k, v, o, dout, dq, dk, dv are contiguous bf16 [B, H, N, d] on the GPU
+(d in {64, 128}); lse is fp32 [B, H, N]; kv_len is int32 [B] on the GPU.
+"""
+
+import math
+
+from . import _lib
+
+__all__ = [
+    "fa_forward",
+    "fa_backward",
+    "fa_backward_workspace_size",
+    "forward",
+    "backward",
+    "FAError",
+]
+
+FAError = _lib.FAError
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _check_qkv(name, t, shape=None):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_lse(t, shape):
+    torch = _torch()
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape[:3]) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"lse must be a contiguous fp32 GPU tensor of shape {tuple(shape[:3])}")
+
+
+def _kv_ptr(kv_len, B, device):
+    torch = _torch()
+    if kv_len is None:
+        return None
+    if kv_len.dtype != torch.int32 or kv_len.dim() != 1 or kv_len.numel() != B or not kv_len.is_cuda:
+        raise ValueError("kv_len must be an int32 GPU tensor of shape [B]")
+    if kv_len.device != device:
+        raise ValueError("kv_len must live on the same device as q")
+    return kv_len.contiguous().data_ptr()
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def fa_forward(q, k, v, o, lse, scale, causal, kv_len=None, stream=None):
+    """C ``fa_forward`` / ``fa_forward_kvlen``: fills o (bf16) and lse (fp32) in place."""
+    _check_qkv("q", q)
+    shape = tuple(q.shape)
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        _check_qkv(name, t, shape)
+    _check_lse(lse, shape)
+    B, H, N, d = shape
+    lib = _lib.load()
+    kvp = _kv_ptr(kv_len, B, q.device)
+    sp = _stream_ptr(stream, q.device)
+    if kvp is None:
+        st = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                            float(scale), int(bool(causal)), sp)
+        _lib.check(st, "fa_forward")
+    else:
+        st = lib.fa_forward_kvlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N,
+                                  d, float(scale), int(bool(causal)), kvp, sp)
+        _lib.check(st, "fa_forward_kvlen")
+
+
+def fa_backward_workspace_size(B, H, N, d):
+    """C ``fa_backward_workspace_size``."""
+    return int(_lib.load().fa_backward_workspace_size(B, H, N, d))
+
+
+def fa_backward(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len=None, stream=None):
+    """C ``fa_backward`` / ``fa_backward_kvlen``: fills dq, dk, dv (bf16) in place.
+
+    workspace: a GPU tensor (any dtype) of at least fa_backward_workspace_size bytes.
+    """
+    _check_qkv("q", q)
+    shape = tuple(q.shape)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_qkv(name, t, shape)
+    _check_lse(lse, shape)
+    B, H, N, d = shape
+    lib = _lib.load()
+    nbytes = workspace.numel() * workspace.element_size()
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    kvp = _kv_ptr(kv_len, B, q.device)
+    sp = _stream_ptr(stream, q.device)
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal))]
+    if kvp is None:
+        st = lib.fa_backward(*args, workspace.data_ptr(), nbytes, sp)
+        _lib.check(st, "fa_backward")
+    else:
+        st = lib.fa_backward_kvlen(*args, kvp, workspace.data_ptr(), nbytes, sp)
+        _lib.check(st, "fa_backward_kvlen")
+
+
+def _default_scale(d, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal=False, scale=None, kv_len=None):
+    """Allocate o and lse, run the fused forward; returns (o, lse)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_forward(q, k, v, o, lse, _default_scale(d, scale), causal, kv_len=kv_len)
+    return o, lse
+
+
+def backward(q, k, v, o, dout, lse, causal=False, scale=None, kv_len=None, workspace=None):
+    """Allocate dq, dk, dv (and a workspace unless given), run the backward."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(q)
+    dv = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(fa_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
+    fa_backward(q, k, v, o, dout, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace, kv_len=kv_len)
+    return dq, dk, dv

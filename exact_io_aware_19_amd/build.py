@@ -1,0 +1,88 @@
+"""Build libfa355.so in-tree with hipcc for gfx950.
+
+    python -m exact_io_aware_19_amd.build [--verbose]
+
+Each source is compiled separately (parallel), then linked into one shared library
+next to this file.  Kernel resource usage (VGPR/AGPR/LDS/spills) is written to
+``_build/resource_usage.txt`` for inspection.
+"""
+
+import argparse
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+BUILD_DIR = os.path.join(PKG_DIR, "_build")
+LIB_NAME = "libfa355.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ARCH = "gfx950"
+
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+
+COMMON_FLAGS = [
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    f"--offload-arch={ARCH}",
+    # packed fp32 VALU forms are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _hipcc():
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm required to build the HIP library)")
+
+
+def _compile(src, verbose):
+    obj = os.path.join(BUILD_DIR, src + ".o")
+    cmd = [_hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".hip"):
+        cmd += ["-Rpass-analysis=kernel-resource-usage"]
+    else:
+        cmd = [_hipcc(), "-x", "hip", *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose:
+        print(" ".join(cmd))
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{r.stderr}")
+    return obj, r.stderr
+
+
+def build(verbose=False):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    objs = [o for o, _ in results]
+    usage = "\n".join(err for _, err in results if "resource usage" in err.lower() or "remark" in err)
+    with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
+        f.write(usage)
+    tmp = LIB_PATH + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking {LIB_NAME} failed:\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}")
+    return LIB_PATH
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    build(verbose=args.verbose)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

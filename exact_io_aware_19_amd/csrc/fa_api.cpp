@@ -1,0 +1,144 @@
+// C ABI of libfa355.so: host-side validation and dispatch.  Every check runs before
+// any HIP call, so invalid calls return a negative status on any host (with or
+// without a GPU) and enqueue nothing.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  // B*H*N*d < 2^62 and the 1-D grid (query blocks x heads) fits 2^31
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > (1ull << 30)) return FA_ERR_SHAPE;
+  const unsigned long long elems = bh * (unsigned long long)N * (unsigned long long)d;
+  if (elems >= (1ull << 62)) return FA_ERR_SHAPE;
+  const unsigned long long qblocks = ((unsigned long long)N + 63) / 64;
+  if (qblocks * bh >= (1ull << 31)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float scale) { return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                 float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u)) return FA_ERR_ALIGN;
+  fa355::FwdArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.kv_len = kv_len;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal != 0;
+  return fa355::launch_forward(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t workspace_bytes(int B, int H, int N, int d) {
+  const size_t rows = (size_t)B * H * N;
+  const size_t dsum = (rows * 4 + 255) & ~(size_t)255;
+  const size_t acc = (rows * (size_t)d * 4 + 255) & ~(size_t)255;
+  return dsum + acc;
+}
+
+int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                  const int32_t* kv_len, void* workspace, size_t ws_bytes, fa_stream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if (!workspace || ws_bytes < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) || ((uintptr_t)workspace & 255u))
+    return FA_ERR_ALIGN;
+  fa355::BwdArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.kv_len = kv_len;
+  const size_t rows = (size_t)B * H * N;
+  a.dsum = (float*)workspace;
+  a.dq_acc = (float*)((char*)workspace + ((rows * 4 + 255) & ~(size_t)255));
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal != 0;
+  return fa355::launch_backward(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, fa_stream_t stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, stream);
+}
+
+int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                     float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, kv_len, stream);
+}
+
+size_t fa_backward_workspace_size(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  return workspace_bytes(B, H, N, d);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
+                size_t workspace_bytes_, fa_stream_t stream) {
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, nullptr, workspace,
+                       workspace_bytes_, stream);
+}
+
+int fa_backward_kvlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                      const int32_t* kv_len, void* workspace, size_t workspace_bytes_, fa_stream_t stream) {
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, kv_len, workspace,
+                       workspace_bytes_, stream);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N < 1, or the problem is too large";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dim must be 64 or 128";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned (lse 4, workspace 256)";
+    default: return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

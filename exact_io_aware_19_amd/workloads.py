@@ -1,0 +1,170 @@
+"""Seeded synthetic workloads shaped like the pages' evaluations.
+
+This module only draws inputs; it holds none of the attention arithmetic.  It serves
+both the GPU path (bf16 bit patterns) and the fp64 oracle (the exact values of those
+same bf16 numbers), so both sides always see identical inputs.
+
+Shapes stand in for the pages' evaluation workloads (singularity-lens FA1 explainer,
+evaluation and results paragraphs: BERT-large, GPT-2, long-context up to 64K tokens;
+"FlashAttention" wiki page, FA1: Path-256 at 64K).  No dataset or trained weight is
+used: every tensor is i.i.d. N(0, 1) drawn in fp32 from numpy's PCG64 and rounded to
+bf16 (round to nearest, ties to even).
+
+Draw order per workload (one generator per workload seed): q, k, v (each
+[B, H, N, d] float32), then dO, then the key-padding lengths, then the indices of
+the key rows scaled x8, then the sampled query rows.
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "get_workload",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f64",
+    "generate",
+]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    scale: float
+    seed: int
+    kv_len_range: tuple = None     # (lo, hi) inclusive, per-batch key padding
+    scaled_key_frac: float = 0.0   # fraction of key rows multiplied by 8 (same rows in every head)
+    sampled_rows: int = 0          # oracle checks only these query rows (0 = all)
+    backward: bool = True
+    note: str = ""
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+    def fwd_flops(self):
+        """4 B H N^2 d, halved when causal (the convention of the throughput metric)."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self):
+        return 2.5 * self.fwd_flops()
+
+
+def _sweep(n, causal):
+    return Workload(
+        name=f"sweep_n{n}_{'causal' if causal else 'full'}", B=2, H=16, N=n, d=128, causal=causal,
+        scale=1.0 / math.sqrt(128), seed=1040 + int(math.log2(n)),
+        note="large-head throughput sweep; the same inputs for both mask modes")
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 128, 64, False, 1.0 / 8, 1001, note="tiny forward+backward"),
+    "bert_large": Workload("bert_large", 8, 16, 512, 64, False, 1.0 / 8, 1002, kv_len_range=(256, 512),
+                           note="BERT-large-shaped, per-batch key padding"),
+    "gpt2": Workload("gpt2", 8, 12, 1024, 64, True, 1.0 / 8, 1003, note="GPT-2-shaped causal"),
+    **{w.name: w for n in (2048, 4096, 8192, 16384) for w in (_sweep(n, False), _sweep(n, True))},
+    "long_64k": Workload("long_64k", 1, 16, 65536, 64, True, 1.0 / 8, 1005, scaled_key_frac=0.01,
+                         sampled_rows=64, backward=False,
+                         note="long-context causal forward; 1% of key rows x8; 64 sampled query rows"),
+}
+
+
+def get_workload(name):
+    return WORKLOADS[name]
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f64(bits):
+    """Exact float64 values of bf16 bit patterns."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+@dataclass
+class Inputs:
+    workload: Workload
+    q: np.ndarray          # uint16 bf16 bits [B,H,N,d]
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray = None
+    kv_len: np.ndarray = None        # int32 [B] or None
+    scaled_keys: np.ndarray = None   # int64 indices of key rows multiplied by 8
+    rows: np.ndarray = None          # sampled query rows (sorted) or None = all
+    extra: dict = field(default_factory=dict)
+
+    def head64(self, name, b, h):
+        """fp64 values of one head of tensor `name` ('q','k','v','do')."""
+        return bf16_bits_to_f64(getattr(self, name)[b, h])
+
+    def to_torch(self, device):
+        """bf16 torch tensors (and int32 kv_len) on `device`."""
+        import torch
+
+        def t(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+
+        out = {"q": t(self.q), "k": t(self.k), "v": t(self.v)}
+        if self.do is not None:
+            out["do"] = t(self.do)
+        out["kv_len"] = None if self.kv_len is None else torch.from_numpy(self.kv_len.astype(np.int32)).to(device)
+        return out
+
+
+def generate(w, with_do=None, shape_override=None):
+    """Draw the inputs of workload `w` (a Workload or its name).
+
+    shape_override=(B,H,N,d) draws a smaller instance with the same recipe (used by
+    tests that need several tiles and a ragged tail at oracle-friendly sizes)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    B, H, N, d = shape_override or w.shape
+    rng = np.random.default_rng(w.seed)
+    qf = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    kf = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    vf = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    if with_do is None:
+        with_do = w.backward
+    dof = rng.standard_normal((B, H, N, d), dtype=np.float32) if with_do else None
+    kv_len = None
+    if w.kv_len_range is not None:
+        lo, hi = w.kv_len_range
+        lo, hi = min(lo, N), min(hi, N)
+        kv_len = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    scaled = None
+    if w.scaled_key_frac > 0:
+        nsc = max(1, int(math.floor(w.scaled_key_frac * N)))
+        scaled = np.sort(rng.choice(N, size=nsc, replace=False))
+        kf[:, :, scaled, :] *= 8.0  # exact in bf16
+    rows = None
+    if w.sampled_rows:
+        rows = np.sort(rng.choice(N, size=min(w.sampled_rows, N), replace=False))
+    return Inputs(
+        workload=w,
+        q=f32_to_bf16_bits(qf),
+        k=f32_to_bf16_bits(kf),
+        v=f32_to_bf16_bits(vf),
+        do=None if dof is None else f32_to_bf16_bits(dof),
+        kv_len=kv_len,
+        scaled_keys=scaled,
+        rows=rows,
+    )

@@ -1,0 +1,109 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa355.so).
+ *
+ * The library computes exact scaled-dot-product attention
+ *
+ *     O = softmax(scale * Q K^T [+ mask]) V
+ *
+ * in one fused forward kernel that streams K/V tiles through LDS and keeps a running
+ * row maximum and row sum (online softmax), so the N x N score matrix never reaches
+ * HBM; the backward pass recomputes the probabilities on chip from the saved per-row
+ * log-sum-exp instead of storing them.  Sources: "FlashAttention" concept wiki page
+ * (notes.yuuk.io), section 定義 -- tiling with online softmax (1) and recomputation in
+ * the backward (2), exact result, O(N) extra memory; singularity-lens FA1 explainer,
+ * paragraphs on tiling, on the online softmax and on recomputation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors q, k, v, o, dout, dq, dk, dv are DEVICE pointers to contiguous row-major
+ *    [B][H][N][d] arrays of bfloat16 (IEEE binary32 upper halves, stored as uint16).
+ *    Rows must be 16-byte aligned (true for any hipMalloc'd base since d*2 is a
+ *    multiple of 16).
+ *  - lse is a DEVICE pointer to a contiguous [B][H][N] float32 array holding, per query
+ *    row, the natural-log log-sum-exp of that row's scaled, masked scores
+ *    (-inf for a row with no admissible key).
+ *  - kv_len (the *_kvlen variants) is a DEVICE pointer to int32[B]; for batch b only
+ *    keys j < kv_len[b] are attended (values are clamped to [0, N]).  NULL = no padding.
+ *  - causal != 0: query i attends keys j <= i (square problem, the same N for queries
+ *    and keys).  Both masks may be combined.
+ *  - scale must be finite and > 0 (it multiplies Q K^T before the softmax).
+ *  - Supported head dims: d = 64 and d = 128.  Any N >= 1, B >= 1, H >= 1 with
+ *    B*H*N*d < 2^62.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    synchronises; it only enqueues kernels on `stream` (0 = the null stream) and
+ *    returns.  Execution faults surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call; an invalid call
+ *    returns a negative fa_status and enqueues nothing.  A failed launch returns
+ *    FA_ERR_LAUNCH.  There is no global mutable state: calls on different streams
+ *    may run concurrently.
+ */
+#ifndef FA355_FA_H
+#define FA355_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* fa_stream_t; /* identical to hipStream_t */
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = -2,     /* B, H or N < 1, or the element count overflows        */
+  FA_ERR_HEADDIM = -3,   /* d is not 64 or 128                                   */
+  FA_ERR_SCALE = -4,     /* scale is not finite or not > 0                        */
+  FA_ERR_WORKSPACE = -5, /* backward workspace NULL or smaller than required     */
+  FA_ERR_LAUNCH = -6,    /* a kernel launch failed (hipGetLastError)             */
+  FA_ERR_ALIGN = -7      /* a tensor pointer is not 16-byte aligned              */
+} fa_status;
+
+/*
+ * Forward pass.  Writes o [B][H][N][d] (bf16) and lse [B][H][N] (fp32).
+ * Operation: exact attention with online softmax over K/V tiles ("FlashAttention"
+ * wiki page, 定義 (1); FA1 explainer, tiling and online-softmax paragraphs).
+ * Inputs q, k, v are read only; o and lse are overwritten entirely (every row < N).
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, fa_stream_t stream);
+
+/* Forward pass with per-batch key padding (kv_len, device int32[B]); otherwise as fa_forward. */
+int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                     float scale, int causal, const int32_t* kv_len, fa_stream_t stream);
+
+/*
+ * Size in bytes of the device workspace fa_backward needs: one fp32 per query row for
+ * D_i = sum_k dO_ik O_ik plus one fp32 [B][H][N][d] accumulator for dQ, rounded up to
+ * 256 bytes.  Returns 0 for invalid sizes.
+ */
+size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass: gradients of L = sum(O * dout) with respect to q, k and v.
+ * P is recomputed on chip from q, k and the forward's lse (no N x N matrix is stored:
+ * "FlashAttention" wiki page, 定義 (2); FA1 explainer, recomputation paragraph).
+ * o and lse must be the outputs of fa_forward on the same q, k, v, scale and masks.
+ * Writes dq, dk, dv [B][H][N][d] (bf16) entirely; keys masked out for every query
+ * (padding) get exact zeros in dk and dv.  workspace: device buffer of at least
+ * fa_backward_workspace_size(B,H,N,d) bytes, 256-byte aligned, owned by the caller;
+ * its contents on entry are ignored and on return are unspecified.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
+                size_t workspace_bytes, fa_stream_t stream);
+
+/* Backward pass with per-batch key padding (kv_len, device int32[B]); otherwise as fa_backward. */
+int fa_backward_kvlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                      const int32_t* kv_len, void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_FA_H */

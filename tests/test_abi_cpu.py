@@ -1,0 +1,105 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point declared in
+include/fa.h, and rejects invalid arguments with the documented status before any HIP
+call (so these run on a host without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_19_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared():
+    with open(HEADER) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fa_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail(f"{_lib.LIB_PATH} not built; run python -m exact_io_aware_19_amd.build")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.fa_status_string(code).decode().startswith(name)
+    assert lib.fa_status_string(12345).decode() == "unknown fa_status"
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on error paths
+
+
+def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, scale=0.125, causal=0):
+    return lib.fa_forward(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+        (dict(B=0), -2), (dict(H=0), -2), (dict(N=0), -2), (dict(N=-5), -2), (dict(B=1 << 20, H=1 << 11), -2),
+        (dict(d=96), -3), (dict(d=0), -3), (dict(d=256), -3),
+        (dict(scale=0.0), -4), (dict(scale=-1.0), -4), (dict(scale=float("inf")), -4), (dict(scale=float("nan")), -4),
+        (dict(q=FAKE + 8), -7), (dict(lse=FAKE + 2), -7),
+    ],
+)
+def test_forward_rejects(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+def test_forward_kvlen_rejects(lib):
+    assert lib.fa_forward_kvlen(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 0.1, 0, FAKE, None) == -1
+    assert lib.fa_forward_kvlen(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 80, 0.1, 0, FAKE, None) == -3
+
+
+def test_workspace_size(lib):
+    B, H, N, d = 2, 3, 100, 128
+    rows = B * H * N
+    want = ((rows * 4 + 255) // 256) * 256 + ((rows * d * 4 + 255) // 256) * 256
+    assert lib.fa_backward_workspace_size(B, H, N, d) == want
+    assert lib.fa_backward_workspace_size(0, H, N, d) == 0
+    assert lib.fa_backward_workspace_size(B, H, N, 72) == 0
+
+
+def _bwd(lib, ws=FAKE, ws_bytes=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=1, N=16, d=64,
+             scale=0.125, causal=0)
+    a.update(kw)
+    need = lib.fa_backward_workspace_size(a["B"], a["H"], a["N"], a["d"]) if a["N"] > 0 else 0
+    return lib.fa_backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                           a["H"], a["N"], a["d"], a["scale"], a["causal"], ws,
+                           need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"])
+def test_backward_rejects_null(lib, missing):
+    assert _bwd(lib, **{missing: None}) == -1
+
+
+def test_backward_rejects_bad_args(lib):
+    assert _bwd(lib, d=32) == -3
+    assert _bwd(lib, N=0) == -2
+    assert _bwd(lib, scale=0.0) == -4
+    assert _bwd(lib, ws=None) == -5
+    assert _bwd(lib, ws_bytes=16) == -5
+    assert _bwd(lib, ws=FAKE + 16) == -7
+    assert _bwd(lib, dq=FAKE + 4) == -7
+    assert lib.fa_backward_kvlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 0.1, 0, FAKE,
+                                 None, 0, None) == -5
