@@ -39,13 +39,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// acc + lo(w) + hi(w) for a dword of two bf16 (v_dot2c_f32_bf16 against (1, 1)): sums
-// exactly the rounded values that feed the MFMA.
-__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
@@ -97,5 +90,123 @@ __device__ __forceinline__ void g2lds16(const void* gptr, unsigned char* lds_wav
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------
+// Tiles of ROWS rows x D head-dims (bf16) staged in LDS.
+//
+// Natural tile: [ROWS][D], 16-byte chunk c of row r stored at chunk c ^ swz_nat<D>(r).
+// It is filled by direct global->LDS copies and read as MFMA operands whose 32 lanes
+// take 32 different rows at one logical chunk; the swizzle puts any 16 consecutive rows
+// on 16 distinct 16-byte bank groups.
+//
+// Transposed tile: [D][ROWS], row = head-dim index, 8 consecutive tile rows per
+// 16-byte chunk, chunk c of row d stored at c ^ swz_tr<ROWS>(d).  Filled through
+// registers (4x4 bf16 blocks transposed with v_perm) and read as MFMA operands whose
+// lanes take 16 consecutive d at one chunk; the swizzle keeps both conflict-free.
+// ---------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ uint32_t swz_nat(uint32_t row) {
+  if constexpr (D == 128) return row & 15u;
+  else return (row >> 1) & 7u;
+}
+template <int ROWS>
+__device__ __forceinline__ uint32_t swz_tr(uint32_t d) {
+  if constexpr (ROWS == 64) return ((d >> 1) + (d >> 4)) & 7u;
+  else return (d + (d >> 4)) & 15u;
+}
+template <int D>
+__device__ __forceinline__ uint32_t nat_offset(uint32_t row, uint32_t chunk) {
+  return row * (D * 2) + ((chunk ^ swz_nat<D>(row)) * 16);
+}
+template <int ROWS>
+__device__ __forceinline__ uint32_t tr_offset(uint32_t d, uint32_t chunk) {
+  return d * (ROWS * 2) + ((chunk ^ swz_tr<ROWS>(d)) * 16);
+}
+
+// Row of a 32-row block that lane c feeds as the A operand: bits 2 and 3 of c swapped.
+// With it, C register r of lane l belongs to block row 16*(r/8) + 8*(l/32) + (r%8), so
+// each lane's eight consecutive C registers are eight consecutive rows -- the k-slots
+// that lane feeds when the result is used as the B operand of the next product.
+__device__ __forceinline__ uint32_t row_perm(uint32_t c) { return (c & ~12u) | ((c & 4u) << 1) | ((c & 8u) >> 1); }
+// Block row held by C register r of a lane in half h (inverse view of row_perm).
+__device__ __forceinline__ constexpr int c_row(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+
+// Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix into a natural tile.
+// Rows past N are clamped to N-1 (finite data; callers mask them).
+template <int ROWS, int D, int NWAVES>
+__device__ __forceinline__ void load_nat_tile(const uint16_t* g, int row0, int N, unsigned char* tile, int w, int l) {
+  constexpr int CPR = D / 8;
+  constexpr int PER_WAVE = ROWS * CPR / (NWAVES * 64);
+  static_assert(PER_WAVE * NWAVES * 64 == ROWS * CPR, "tile must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int pos = (i * NWAVES + w) * 64 + l;
+    const int row = pos / CPR, pc = pos % CPR;
+    const int lc = pc ^ (int)swz_nat<D>(row);
+    const int grow = min(row0 + row, N - 1);
+    g2lds16(g + (size_t)grow * D + lc * 8, tile + (size_t)(i * NWAVES + w) * 64 * 16);
+  }
+}
+
+// Register-staged transposed tile: fetch() issues the global loads, store() writes the
+// transposed blocks to LDS (after the loads have landed).
+template <int ROWS, int D, int NTHREADS>
+struct TrTile {
+  static constexpr int NBLK = (ROWS / 4) * (D / 4) / NTHREADS;
+  static_assert(NBLK >= 1 && NBLK * NTHREADS == (ROWS / 4) * (D / 4), "tile must split evenly over the threads");
+  u32x2 r[NBLK][4];
+
+  __device__ __forceinline__ void fetch(const uint16_t* g, int row0, int N, int tid) {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+      const int vb = tid + i * NTHREADS;
+      const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
+      const int k0 = kc * 8 + hsel * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int grow = min(row0 + k0 + j, N - 1);
+        r[i][j] = *(const u32x2*)(g + (size_t)grow * D + dq * 4);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+      const int vb = tid + i * NTHREADS;
+      const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // column j of the 4x4 block: (X[k0..k0+3][4*dq + j])
+        const int half = j >> 1;
+        u32x2 out;
+        if (j & 1) {
+          out[0] = hi16_pair(r[i][0][half], r[i][1][half]);
+          out[1] = hi16_pair(r[i][2][half], r[i][3][half]);
+        } else {
+          out[0] = lo16_pair(r[i][0][half], r[i][1][half]);
+          out[1] = lo16_pair(r[i][2][half], r[i][3][half]);
+        }
+        const uint32_t d = dq * 4 + j;
+        lds_write64(tile, d * (ROWS * 2) + ((kc ^ swz_tr<ROWS>(d)) * 16) + hsel * 8, out);
+      }
+    }
+  }
+};
+
+// Store a C fragment holding X^T (rows = head-dim d, column = this lane's row `row`)
+// as bf16 row `row` of a [N][D] matrix, scaled by `mul`.
+template <int D>
+__device__ __forceinline__ void store_ct_rows(uint16_t* g, int row, const f32x16 (&acc)[D / 32], float mul, int h) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d0 = 32 * db + 8 * gq + 4 * h;
+      u32x2 out;
+      out[0] = pack_bf16x2(acc[db][4 * gq + 0] * mul, acc[db][4 * gq + 1] * mul);
+      out[1] = pack_bf16x2(acc[db][4 * gq + 2] * mul, acc[db][4 * gq + 3] * mul);
+      *(u32x2*)(g + (size_t)row * D + d0) = out;
+    }
+}
 
 }  // namespace fa355

@@ -52,10 +52,9 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 }
 
 size_t workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
   const size_t rows = (size_t)B * H * N;
-  const size_t dsum = (rows * 4 + 255) & ~(size_t)255;
-  const size_t acc = (rows * (size_t)d * 4 + 255) & ~(size_t)255;
-  return dsum + acc;
+  return (rows * 4 + 255) & ~(size_t)255;  // D_i = rowsum(dO * O), fp32 [B][H][N]
 }
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -81,9 +80,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
   a.kv_len = kv_len;
-  const size_t rows = (size_t)B * H * N;
   a.dsum = (float*)workspace;
-  a.dq_acc = (float*)((char*)workspace + ((rows * 4 + 255) & ~(size_t)255));
   a.B = B;
   a.H = H;
   a.N = N;

@@ -27,40 +27,16 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
 
-// K tile in LDS: [BN][D] bf16, 16-byte chunk c of row r stored at chunk c ^ swz_k(r).
-// Reads (MFMA A operand) hit 16 consecutive rows at one logical chunk; the swizzle
-// spreads them over 16 distinct 16-byte bank groups.
-template <int D>
-__device__ __forceinline__ uint32_t swz_k(uint32_t row) {
-  if constexpr (D == 128) return row & 15u;
-  else return (row >> 1) & 7u;
-}
-
-// V^T tile in LDS: [D][BN] bf16 (row = head-dim index, 8 keys per 16-byte chunk).
-// Reads hit 16 consecutive rows at one chunk; the 4x4-block transposed writes hit rows
-// spaced by 4 -- the swizzle keeps both conflict-free.
-template <int BN>
-__device__ __forceinline__ uint32_t swz_v(uint32_t d) {
-  if constexpr (BN == 64) return ((d >> 1) + (d >> 4)) & 7u;
-  else return (d + (d >> 4)) & 15u;
-}
-
-// Row of K that lane c of the A operand supplies inside a 32-key block: bits 2 and 3
-// of c swapped.  With it, score register r of lane (h = l/32) belongs to key
-// 16*(r/8) + 8*h + (r%8), so each lane's eight consecutive score registers are eight
-// consecutive keys -- exactly the k-slots that lane feeds to the P V^T product.
-__device__ __forceinline__ uint32_t key_perm(uint32_t c) { return (c & ~12u) | ((c & 4u) << 1) | ((c & 8u) >> 1); }
-
 template <int D, int BN, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  constexpr int KT_BYTES = BN * D * 2;  // one K tile, one V^T tile
-  constexpr int NKB = BN / 32;          // 32-key blocks per tile
-  constexpr int NDB = D / 32;           // 32-row blocks of the head dim
-  constexpr int NKK = D / 16;           // k-steps of the QK^T contraction
-  // LDS: K tiles at [0, 2*KT_BYTES), V^T tiles at [2*KT_BYTES, 4*KT_BYTES)
-  auto kbuf = [&](int i) { return smem + i * KT_BYTES; };
-  auto vbuf = [&](int i) { return smem + (2 + i) * KT_BYTES; };
+  constexpr int TILE_BYTES = BN * D * 2;  // one K tile or one V^T tile
+  constexpr int NKB = BN / 32;            // 32-key blocks per tile
+  constexpr int NDB = D / 32;             // 32-row blocks of the head dim
+  constexpr int NKK = D / 16;             // k-steps of the QK^T contraction
+  // LDS: K tiles (natural) at [0, 2*TILE_BYTES), V^T tiles at [2*TILE_BYTES, 4*TILE_BYTES)
+  auto kbuf = [&](int i) { return smem + i * TILE_BYTES; };
+  auto vbuf = [&](int i) { return smem + (2 + i) * TILE_BYTES; };
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
@@ -84,9 +60,20 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   int kend = kv_end;
   if constexpr (CAUSAL) kend = min(kend, q0 + kBM);
   const int ntiles = (kend + BN - 1) / BN;
-  // last key any row of this wave may attend (exclusive bound for tile skipping)
+  // keys past wave_kend are masked for every row of this wave (tile skipping)
   int wave_kend = kend;
   if constexpr (CAUSAL) wave_kend = min(kend, q0 + w * kRowsPerWave + kRowsPerWave);
+
+  if (ntiles == 0) {  // no admissible key for any row of this block (kv_len == 0)
+    if (qrow < N) {
+      f32x16 zero[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) zero[db] = f32x16{};
+      store_ct_rows<D>(p.o + head, qrow, zero, 0.f, h);
+      if (h == 0) p.lse[(size_t)bh * N + qrow] = -INFINITY;
+    }
+    return;
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers for the whole kernel
   u32x4 qf[NKK];
@@ -107,92 +94,21 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   float l_run = 0.f;        // this lane's partial row sum (the other half-wave holds the rest)
   const float sl = p.scale_log2;
 
-  // ---- tile loaders -------------------------------------------------------------
-  // K: direct global->LDS copies, 16 B per lane, swizzle applied on the global side.
-  auto load_k = [&](int tile, unsigned char* dst) {
-    constexpr int CPR = D / 8;                       // 16-byte chunks per row
-    constexpr int CHUNKS = BN * CPR;                 // per tile
-    constexpr int PER_WAVE = CHUNKS / (kWaves * 64); // wave instructions
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int pos = (i * kWaves + w) * 64 + l;  // LDS chunk position
-      const int row = pos / CPR, pc = pos % CPR;
-      const int lc = pc ^ swz_k<D>(row);
-      const int grow = min(tile * BN + row, N - 1);
-      g2lds16(kg + (size_t)grow * D + lc * 8, dst + (size_t)(i * kWaves + w) * 64 * 16);
-    }
-  };
-  // V: 4 keys x 4 head-dims per thread through registers, written transposed.
-  constexpr int VBLK = (BN / 4) * (D / 4) / kThreads;  // 4x4 blocks per thread
-  static_assert(VBLK >= 1, "tile too small");
-  u32x2 vr[VBLK][4];
-  auto fetch_v = [&](int tile) {
-#pragma unroll
-    for (int i = 0; i < VBLK; ++i) {
-      const int vb = tid + i * kThreads;
-      const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
-      const int k0 = kc * 8 + hsel * 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int grow = min(tile * BN + k0 + r, N - 1);
-        vr[i][r] = *(const u32x2*)(vg + (size_t)grow * D + dq * 4);
-      }
-    }
-  };
-  auto store_vt = [&](unsigned char* dst) {
-#pragma unroll
-    for (int i = 0; i < VBLK; ++i) {
-      const int vb = tid + i * kThreads;
-      const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // column j of the 4x4 block: (V[k0..k0+3][d0+j])
-        const uint32_t w0 = (j < 2) ? vr[i][0][0] : vr[i][0][1];
-        const uint32_t w1 = (j < 2) ? vr[i][1][0] : vr[i][1][1];
-        const uint32_t w2 = (j < 2) ? vr[i][2][0] : vr[i][2][1];
-        const uint32_t w3 = (j < 2) ? vr[i][3][0] : vr[i][3][1];
-        u32x2 out;
-        if (j & 1) {
-          out[0] = hi16_pair(w0, w1);
-          out[1] = hi16_pair(w2, w3);
-        } else {
-          out[0] = lo16_pair(w0, w1);
-          out[1] = lo16_pair(w2, w3);
-        }
-        const uint32_t d = dq * 4 + j;
-        const uint32_t byte = d * (BN * 2) + ((kc ^ swz_v<BN>(d)) * 16) + hsel * 8;
-        lds_write64(dst, byte, out);
-      }
-    }
-  };
+  TrTile<BN, D, kThreads> vt;
 
-  if (ntiles == 0) {  // no admissible key for any row of this block (kv_len == 0)
-    if (qrow < N) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * db + 8 * g + 4 * h;
-          *(u32x2*)(p.o + head + (size_t)qrow * D + d0) = u32x2{0, 0};
-        }
-      if (h == 0) p.lse[(size_t)bh * N + qrow] = -INFINITY;
-    }
-    return;
-  }
-
-  // ---- prologue: tile 0 -------------------------------------------------------------
-  load_k(0, kbuf(0));
-  fetch_v(0);
+  // ---- prologue: tile 0
+  load_nat_tile<BN, D, kWaves>(kg, 0, N, kbuf(0), w, l);
+  vt.fetch(vg, 0, N, tid);
   wait_vmem();
-  store_vt(vbuf(0));
+  vt.store(vbuf(0), tid);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
     const bool has_next = t + 1 < ntiles;
     if (has_next) {
-      load_k(t + 1, kbuf(cur ^ 1));
-      fetch_v(t + 1);
+      load_nat_tile<BN, D, kWaves>(kg, (t + 1) * BN, N, kbuf(cur ^ 1), w, l);
+      vt.fetch(vg, (t + 1) * BN, N, tid);
     }
     const int kt0 = t * BN;
     if (kt0 < wave_kend) {
@@ -202,11 +118,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = f32x16{};
-        const uint32_t row = 32 * kb + key_perm(c);
+        const uint32_t row = 32 * kb + row_perm(c);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const uint32_t lc = 2 * kk + h;
-          const u32x4 a = lds_read128(kb_, row * (D * 2) + ((lc ^ swz_k<D>(row)) * 16));
+          const u32x4 a = lds_read128(kb_, nat_offset<D>(row, 2 * kk + h));
           s[kb] = mfma32(a, qf[kk], s[kb]);
         }
       }
@@ -218,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
+            const int key = kt0 + 32 * kb + c_row(r, h);
             bool bad = key >= kv_end;
             if constexpr (CAUSAL) bad = bad || key > qrow;
             if (bad) s[kb][r] = -INFINITY;
@@ -258,18 +173,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          const uint32_t lc = 4 * kb + 2 * sb + h;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const uint32_t d = 32 * db + c;
-            const u32x4 a = lds_read128(vb_, d * (BN * 2) + ((lc ^ swz_v<BN>(d)) * 16));
+            const u32x4 a = lds_read128(vb_, tr_offset<BN>(32 * db + c, 4 * kb + 2 * sb + h));
             o[db] = mfma32(a, pk[kb][sb], o[db]);
           }
         }
     }
     if (has_next) {
       wait_vmem();
-      store_vt(vbuf(cur ^ 1));
+      vt.store(vbuf(cur ^ 1), tid);
     }
     __syncthreads();
   }
@@ -279,16 +192,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   if (qrow < N) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;
-        u32x2 out;
-        out[0] = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
-        out[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(u32x2*)(p.o + head + (size_t)qrow * D + d0) = out;
-      }
+    store_ct_rows<D>(p.o + head, qrow, o, inv, h);
     if (h == 0) p.lse[(size_t)bh * N + qrow] = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
   }
 }
@@ -297,12 +201,8 @@ template <int D, int BN, bool CAUSAL, bool KVLEN>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   constexpr size_t lds = 4ull * BN * D * 2;
   auto kern = fa_fwd_kernel<D, BN, CAUSAL, KVLEN>;
-  static bool attr_set = false;  // idempotent attribute, racing writers store the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   const int nqb = (a.N + kBM - 1) / kBM;
   const unsigned grid = (unsigned)nqb * (unsigned)(a.B * a.H);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a);

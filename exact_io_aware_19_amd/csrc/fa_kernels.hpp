@@ -29,7 +29,6 @@ struct BwdArgs {
   uint16_t* dv;
   const int32_t* kv_len;  // device int32[B] or nullptr
   float* dsum;            // workspace: D_i = rowsum(dO * O), fp32 [B][H][N]
-  float* dq_acc;          // workspace: fp32 [B][H][N][d] dQ accumulator
   int B, H, N, d;
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)

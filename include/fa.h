@@ -75,8 +75,9 @@ int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Size in bytes of the device workspace fa_backward needs: one fp32 per query row for
- * D_i = sum_k dO_ik O_ik plus one fp32 [B][H][N][d] accumulator for dQ, rounded up to
- * 256 bytes.  Returns 0 for invalid sizes.
+ * D_i = sum_k dO_ik O_ik (4*B*H*N bytes, rounded up to 256).  dQ needs no accumulator:
+ * it is produced by a query-outer pass that keeps its rows in registers.  Returns 0 for
+ * invalid sizes.
  */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
 
@@ -86,7 +87,8 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d);
  * "FlashAttention" wiki page, 定義 (2); FA1 explainer, recomputation paragraph).
  * o and lse must be the outputs of fa_forward on the same q, k, v, scale and masks.
  * Writes dq, dk, dv [B][H][N][d] (bf16) entirely; keys masked out for every query
- * (padding) get exact zeros in dk and dv.  workspace: device buffer of at least
+ * (padding) get exact zeros in dk and dv.  No atomics are used: the results are
+ * bitwise reproducible run to run.  workspace: device buffer of at least
  * fa_backward_workspace_size(B,H,N,d) bytes, 256-byte aligned, owned by the caller;
  * its contents on entry are ignored and on return are unspecified.
  */

@@ -72,7 +72,7 @@ def test_forward_kvlen_rejects(lib):
 def test_workspace_size(lib):
     B, H, N, d = 2, 3, 100, 128
     rows = B * H * N
-    want = ((rows * 4 + 255) // 256) * 256 + ((rows * d * 4 + 255) // 256) * 256
+    want = ((rows * 4 + 255) // 256) * 256
     assert lib.fa_backward_workspace_size(B, H, N, d) == want
     assert lib.fa_backward_workspace_size(0, H, N, d) == 0
     assert lib.fa_backward_workspace_size(B, H, N, 72) == 0
