@@ -92,35 +92,31 @@ __device__ __forceinline__ void g2lds16(const void* gptr, unsigned char* lds_wav
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------
-// Tiles of ROWS rows x D head-dims (bf16) staged in LDS.
+// LDS tiles, "blocked chunk-major" layout.
 //
-// Natural tile: [ROWS][D], 16-byte chunk c of row r stored at chunk c ^ swz_nat<D>(r).
-// It is filled by direct global->LDS copies and read as MFMA operands whose 32 lanes
-// take 32 different rows at one logical chunk; the swizzle puts any 16 consecutive rows
-// on 16 distinct 16-byte bank groups.
+// A tile is a matrix of R rows, each NCH 16-byte chunks long (8 bf16 per chunk).  The
+// 16-byte unit holding chunk ch of row r sits at
+//     unit(r, ch) = (r / 16) * 16 * NCH  +  ch * 16  +  (r % 16)
+// i.e. blocks of 16 rows, chunk-major inside a block.  MFMA operand reads have 16
+// lanes take 16 consecutive rows at one chunk: 16 consecutive units, one per 16-byte
+// bank group, so they never conflict; and moving to another chunk or another 16-row
+// block adds a compile-time constant, so every fragment address is one per-lane base
+// plus an immediate offset.
 //
-// Transposed tile: [D][ROWS], row = head-dim index, 8 consecutive tile rows per
-// 16-byte chunk, chunk c of row d stored at c ^ swz_tr<ROWS>(d).  Filled through
-// registers (4x4 bf16 blocks transposed with v_perm) and read as MFMA operands whose
-// lanes take 16 consecutive d at one chunk; the swizzle keeps both conflict-free.
+// Natural tile: a [ROWS][D] slice of a row-major [N][D] matrix (NCH = D/8), filled
+// with direct global->LDS copies (each wave instruction fills 64 consecutive units:
+// 16 rows x 4 chunks).
+// Transposed tile: the same slice stored as [D][ROWS] (row = head-dim index, NCH =
+// ROWS/8: 8 consecutive slice rows per chunk), filled through registers with 4x4 bf16
+// blocks transposed by v_perm.
 // ---------------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ uint32_t swz_nat(uint32_t row) {
-  if constexpr (D == 128) return row & 15u;
-  else return (row >> 1) & 7u;
+template <int NCH>
+__device__ __forceinline__ constexpr uint32_t bcm_unit(uint32_t row, uint32_t ch) {
+  return (row >> 4) * (16 * NCH) + ch * 16 + (row & 15);
 }
-template <int ROWS>
-__device__ __forceinline__ uint32_t swz_tr(uint32_t d) {
-  if constexpr (ROWS == 64) return ((d >> 1) + (d >> 4)) & 7u;
-  else return (d + (d >> 4)) & 15u;
-}
-template <int D>
-__device__ __forceinline__ uint32_t nat_offset(uint32_t row, uint32_t chunk) {
-  return row * (D * 2) + ((chunk ^ swz_nat<D>(row)) * 16);
-}
-template <int ROWS>
-__device__ __forceinline__ uint32_t tr_offset(uint32_t d, uint32_t chunk) {
-  return d * (ROWS * 2) + ((chunk ^ swz_tr<ROWS>(d)) * 16);
+template <int NCH>
+__device__ __forceinline__ constexpr uint32_t bcm_byte(uint32_t row, uint32_t ch) {
+  return bcm_unit<NCH>(row, ch) * 16;
 }
 
 // Row of a 32-row block that lane c feeds as the A operand: bits 2 and 3 of c swapped.
@@ -135,21 +131,22 @@ __device__ __forceinline__ constexpr int c_row(int r, int h) { return 16 * (r >>
 // Rows past N are clamped to N-1 (finite data; callers mask them).
 template <int ROWS, int D, int NWAVES>
 __device__ __forceinline__ void load_nat_tile(const uint16_t* g, int row0, int N, unsigned char* tile, int w, int l) {
-  constexpr int CPR = D / 8;
-  constexpr int PER_WAVE = ROWS * CPR / (NWAVES * 64);
-  static_assert(PER_WAVE * NWAVES * 64 == ROWS * CPR, "tile must split evenly over the waves");
+  constexpr int NCH = D / 8;
+  constexpr int UNITS = ROWS * NCH;
+  constexpr int PER_WAVE = UNITS / (NWAVES * 64);
+  static_assert(PER_WAVE * NWAVES * 64 == UNITS, "tile must split evenly over the waves");
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int pos = (i * NWAVES + w) * 64 + l;
-    const int row = pos / CPR, pc = pos % CPR;
-    const int lc = pc ^ (int)swz_nat<D>(row);
+    const int pos = (i * NWAVES + w) * 64 + l;  // unit index written by this lane
+    const int blk = pos / (16 * NCH), rem = pos % (16 * NCH);
+    const int ch = rem >> 4, row = blk * 16 + (rem & 15);
     const int grow = min(row0 + row, N - 1);
-    g2lds16(g + (size_t)grow * D + lc * 8, tile + (size_t)(i * NWAVES + w) * 64 * 16);
+    g2lds16(g + (size_t)grow * D + ch * 8, tile + (size_t)(i * NWAVES + w) * 64 * 16);
   }
 }
 
 // Register-staged transposed tile: fetch() issues the global loads, store() writes the
-// transposed blocks to LDS (after the loads have landed).
+// transposed 4x4 blocks to LDS (after the loads have landed).
 template <int ROWS, int D, int NTHREADS>
 struct TrTile {
   static constexpr int NBLK = (ROWS / 4) * (D / 4) / NTHREADS;
@@ -186,11 +183,30 @@ struct TrTile {
           out[0] = lo16_pair(r[i][0][half], r[i][1][half]);
           out[1] = lo16_pair(r[i][2][half], r[i][3][half]);
         }
-        const uint32_t d = dq * 4 + j;
-        lds_write64(tile, d * (ROWS * 2) + ((kc ^ swz_tr<ROWS>(d)) * 16) + hsel * 8, out);
+        lds_write64(tile, bcm_byte<ROWS / 8>(dq * 4 + j, kc) + hsel * 8, out);
       }
     }
   }
+};
+
+// Per-lane base byte offsets of MFMA A-operand fragments.
+//  natural tile [R][D]: lane (h, c) reads row 32*blk + row_perm(c), chunk 2*kk + h
+//      -> nat_base + blk * NAT_BLK + kk * NAT_KK
+//  transposed tile [D][R]: lane (h, c) reads row d = 32*db + c, chunk 4*rb + 2*sb + h
+//      -> tr_base + db * TR_DB + (4*rb + 2*sb) * TR_CH
+template <int D>
+struct NatFrag {
+  static constexpr int NCH = D / 8;
+  static constexpr uint32_t BLK = 2 * 16 * NCH * 16;  // 32 rows
+  static constexpr uint32_t KK = 2 * 16 * 16;         // 2 chunks
+  __device__ __forceinline__ static uint32_t base(int c, int h) { return bcm_byte<NCH>(row_perm(c), h); }
+};
+template <int R>
+struct TrFrag {
+  static constexpr int NCH = R / 8;
+  static constexpr uint32_t DB = 2 * 16 * NCH * 16;  // 32 head-dim rows
+  static constexpr uint32_t CH = 16 * 16;            // one chunk (8 tile rows)
+  __device__ __forceinline__ static uint32_t base(int c, int h) { return bcm_byte<NCH>(c, h); }
 };
 
 // Store a C fragment holding X^T (rows = head-dim d, column = this lane's row `row`)

@@ -107,6 +107,8 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
   }
   const float sl = p.scale_log2;
   TrTile<BN, D, kDqThreads> kt;
+  const uint32_t nfrag = NatFrag<D>::base(c, h);  // K and V tiles, A operands of S^T and dP^T
+  const uint32_t tfrag = TrFrag<BN>::base(c, h);  // K^T tile, A operand of dQ^T
 
   load_nat_tile<BN, D, kDqWaves>(kg, 0, N, kbuf(0), w, l);
   load_nat_tile<BN, D, kDqWaves>(vg, 0, N, vbuf(0), w, l);
@@ -131,12 +133,12 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         f32x16 s = f32x16{}, dp = f32x16{};
-        const uint32_t row = 32 * kb + row_perm(c);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 ak = lds_read128(kbuf(cur), nat_offset<D>(row, 2 * kk + h));
+          const uint32_t off = nfrag + kb * NatFrag<D>::BLK + kk * NatFrag<D>::KK;
+          const u32x4 ak = lds_read128(kbuf(cur), off);
           s = mfma32(ak, qf[kk], s);
-          const u32x4 av = lds_read128(vbuf(cur), nat_offset<D>(row, 2 * kk + h));
+          const u32x4 av = lds_read128(vbuf(cur), off);
           dp = mfma32(av, dof[kk], dp);
         }
         if (need_mask) {
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const u32x4 a = lds_read128(ktbuf(cur), tr_offset<BN>(32 * db + c, 4 * kb + 2 * sb + h));
+            const u32x4 a = lds_read128(ktbuf(cur), tfrag + db * TrFrag<BN>::DB + (4 * kb + 2 * sb) * TrFrag<BN>::CH);
             dq[db] = mfma32(a, dsk[sb], dq[db]);
           }
       }
@@ -249,21 +251,25 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   const int i_last = (N + BM - 1) / BM;  // exclusive
   const float sl = p.scale_log2;
   TrTile<BM, D, kKvThreads> qt, dot;
+  const uint32_t nfrag = NatFrag<D>::base(c, h);   // Q and dO tiles, A operands of S and dP
+  const uint32_t tfrag = TrFrag<BM>::base(c, h);   // Q^T and dO^T tiles, A operands of dK^T, dV^T
 
-  // row statistics of one query tile -> registers (lse2 = +inf past N gives P = 0)
+  // row statistics of one query tile: raw loads into registers now, converted only when
+  // stored (using a loaded value early would wait on every load in flight)
   float st_lse = 0.f, st_d = 0.f;
   auto fetch_stats = [&](int i0) {
     if (tid < BM) {
-      const int q = i0 + tid;
-      const float ln = q < N ? lseg[q] : -INFINITY;
-      st_lse = (ln == -INFINITY) ? INFINITY : ln * kLog2e;
-      st_d = q < N ? dsg[q] : 0.f;
+      const int q = min(i0 + tid, N - 1);
+      st_lse = lseg[q];
+      st_d = dsg[q];
     }
   };
-  auto store_stats = [&](unsigned char* st) {
+  auto store_stats = [&](unsigned char* st, int i0) {
     if (tid < BM) {
-      ((float*)(st + St::LSE))[tid] = st_lse;
-      ((float*)(st + St::DSUM))[tid] = st_d;
+      // lse2 = +inf (P = 0) for rows past N and for rows with no admissible key
+      const bool live = i0 + tid < N && st_lse != -INFINITY;
+      ((float*)(st + St::LSE))[tid] = live ? st_lse * kLog2e : INFINITY;
+      ((float*)(st + St::DSUM))[tid] = live ? st_d : 0.f;
     }
   };
   auto issue = [&](int i, unsigned char* st) {
@@ -274,15 +280,15 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     dot.fetch(dog, i0, N, tid);
     fetch_stats(i0);
   };
-  auto finish = [&](unsigned char* st) {
+  auto finish = [&](unsigned char* st, int i) {
     wait_vmem();
     qt.store(st + St::QT, tid);
     dot.store(st + St::DOT, tid);
-    store_stats(st);
+    store_stats(st, i * BM);
   };
 
   issue(i_first, stage(0));
-  finish(stage(0));
+  finish(stage(0), i_first);
   __syncthreads();
 
   for (int i = i_first; i < i_last; ++i) {
@@ -293,58 +299,84 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     unsigned char* st = stage(cur);
     // causal: skip tiles whose queries all precede this wave's first key
     if (!CAUSAL || i0 + BM - 1 >= kw0) {
-      const bool need_mask = CAUSAL && (i0 < kw0 + 31);
+      const int qoff0 = i0 + 8 * h - kcol;  // (query - key) of this lane's first row
+      // Software pipeline over the 32-query blocks of the tile: the operand reads of
+      // the next phase are issued before the math of the current one, so LDS latency
+      // hides behind MFMA and VALU work of the same wave (one wave per SIMD here).
+      u32x4 aq[NKK], ad[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        aq[kk] = lds_read128(st + St::Q, nfrag + kk * NatFrag<D>::KK);
+        ad[kk] = lds_read128(st + St::DO, nfrag + kk * NatFrag<D>::KK);
+      }
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
+        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
         f32x16 s = f32x16{}, dp = f32x16{};
-        const uint32_t row = 32 * qb + row_perm(c);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 aq = lds_read128(st + St::Q, nat_offset<D>(row, 2 * kk + h));
-          s = mfma32(aq, kf[kk], s);
-          const u32x4 ad = lds_read128(st + St::DO, nat_offset<D>(row, 2 * kk + h));
-          dp = mfma32(ad, vf[kk], dp);
+          s = mfma32(aq[kk], kf[kk], s);
+          dp = mfma32(ad[kk], vf[kk], dp);
         }
-        u32x4 pk[2], dsk[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          // statistics of the 8 query rows 32*qb + 16*sb + 8*h + 0..7 held by this lane
-          const int rbase = 32 * qb + 16 * sb + 8 * h;
-          const f32x4 la = *(const f32x4*)(st + St::LSE + rbase * 4);
-          const f32x4 lb = *(const f32x4*)(st + St::LSE + rbase * 4 + 16);
-          const f32x4 da = *(const f32x4*)(st + St::DSUM + rbase * 4);
-          const f32x4 dbv = *(const f32x4*)(st + St::DSUM + rbase * 4 + 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r0 = 8 * sb + 2 * e;
-            const float l0 = (e < 2) ? la[2 * e] : lb[2 * e - 4];
-            const float l1 = (e < 2) ? la[2 * e + 1] : lb[2 * e - 3];
-            const float d0 = (e < 2) ? da[2 * e] : dbv[2 * e - 4];
-            const float d1 = (e < 2) ? da[2 * e + 1] : dbv[2 * e - 3];
-            float p0 = fast_exp2(__builtin_fmaf(s[r0], sl, -l0));
-            float p1 = fast_exp2(__builtin_fmaf(s[r0 + 1], sl, -l1));
-            if (need_mask) {
-              const int q = i0 + rbase + 2 * e;
-              if (kcol > q) p0 = 0.f;
-              if (kcol > q + 1) p1 = 0.f;
-            }
-            pk[sb][e] = pack_bf16x2(p0, p1);
-            dsk[sb][e] = pack_bf16x2(p0 * (dp[r0] - d0), p1 * (dp[r0 + 1] - d1));
-          }
-        }
+        // operands of dV^T / dK^T for this block, and statistics of its rows
+        u32x4 ao[2][NDB], at[2][NDB];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const uint32_t dr = 32 * db + c, ch = 4 * qb + 2 * sb + h;
-            const u32x4 ao = lds_read128(st + St::DOT, tr_offset<BM>(dr, ch));
-            dv[db] = mfma32(ao, pk[sb], dv[db]);
-            const u32x4 aq = lds_read128(st + St::QT, tr_offset<BM>(dr, ch));
-            dk[db] = mfma32(aq, dsk[sb], dk[db]);
+            const uint32_t off = tfrag + db * TrFrag<BM>::DB + (4 * qb + 2 * sb) * TrFrag<BM>::CH;
+            ao[sb][db] = lds_read128(st + St::DOT, off);
+            at[sb][db] = lds_read128(st + St::QT, off);
+          }
+        f32x4 lsv[2][2], dsv[2][2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          // the 8 query rows 32*qb + 16*sb + 8*h + 0..7 held by this lane
+          const int rbase = 32 * qb + 16 * sb + 8 * h;
+          lsv[sb][0] = *(const f32x4*)(st + St::LSE + rbase * 4);
+          lsv[sb][1] = *(const f32x4*)(st + St::LSE + rbase * 4 + 16);
+          dsv[sb][0] = *(const f32x4*)(st + St::DSUM + rbase * 4);
+          dsv[sb][1] = *(const f32x4*)(st + St::DSUM + rbase * 4 + 16);
+        }
+        // next block's S/dP operands
+        if (qb + 1 < NQB) {
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            aq[kk] = lds_read128(st + St::Q, nfrag + (qb + 1) * NatFrag<D>::BLK + kk * NatFrag<D>::KK);
+            ad[kk] = lds_read128(st + St::DO, nfrag + (qb + 1) * NatFrag<D>::BLK + kk * NatFrag<D>::KK);
+          }
+        }
+        // P = exp2(S * scale * log2e - LSE * log2e), dS = P * (dP - D)
+        u32x4 pk[2], dsk[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r0 = 8 * sb + 2 * e;
+            const float l0 = lsv[sb][e >> 1][(2 * e) & 3], l1 = lsv[sb][e >> 1][(2 * e + 1) & 3];
+            const float d0 = dsv[sb][e >> 1][(2 * e) & 3], d1 = dsv[sb][e >> 1][(2 * e + 1) & 3];
+            float p0 = fast_exp2(__builtin_fmaf(s[r0], sl, -l0));
+            float p1 = fast_exp2(__builtin_fmaf(s[r0 + 1], sl, -l1));
+            if constexpr (CAUSAL) {
+              // key kcol is admissible for query q iff kcol <= q; qoff = q - kcol
+              const int qoff = qoff0 + 32 * qb + 16 * sb + 2 * e;
+              p0 = (qoff < 0) ? 0.f : p0;
+              p1 = (qoff + 1 < 0) ? 0.f : p1;
+            }
+            pk[sb][e] = pack_bf16x2(p0, p1);
+            dsk[sb][e] = pack_bf16x2(p0 * (dp[r0] - d0), p1 * (dp[r0 + 1] - d1));
+          }
+        // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dv[db] = mfma32(ao[sb][db], pk[sb], dv[db]);
+            dk[db] = mfma32(at[sb][db], dsk[sb], dk[db]);
           }
       }
     }
-    if (has_next) finish(stage(cur ^ 1));
+    if (has_next) finish(stage(cur ^ 1), i + 1);
     __syncthreads();
   }
   if (col_store) {

@@ -95,6 +95,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   const float sl = p.scale_log2;
 
   TrTile<BN, D, kThreads> vt;
+  const uint32_t kfrag = NatFrag<D>::base(c, h);  // K tile, A operand of S^T
+  const uint32_t vfrag = TrFrag<BN>::base(c, h);  // V^T tile, A operand of O^T
 
   // ---- prologue: tile 0
   load_nat_tile<BN, D, kWaves>(kg, 0, N, kbuf(0), w, l);
@@ -118,10 +120,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = f32x16{};
-        const uint32_t row = 32 * kb + row_perm(c);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 a = lds_read128(kb_, nat_offset<D>(row, 2 * kk + h));
+          const u32x4 a = lds_read128(kb_, kfrag + kb * NatFrag<D>::BLK + kk * NatFrag<D>::KK);
           s[kb] = mfma32(a, qf[kk], s[kb]);
         }
       }
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
         for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const u32x4 a = lds_read128(vb_, tr_offset<BN>(32 * db + c, 4 * kb + 2 * sb + h));
+            const u32x4 a = lds_read128(vb_, vfrag + db * TrFrag<BN>::DB + (4 * kb + 2 * sb) * TrFrag<BN>::CH);
             o[db] = mfma32(a, pk[kb][sb], o[db]);
           }
         }
