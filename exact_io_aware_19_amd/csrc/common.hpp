@@ -55,6 +55,35 @@ __device__ __forceinline__ float half_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
 }
 
+// Max / sum of the 16*NB values of NB C fragments as balanced trees (depth log2, not
+// a serial chain).
+template <int NB>
+__device__ __forceinline__ float tree_max(const f32x16 (&v)[NB]) {
+  float t[8 * NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[8 * b + i] = fmaxf(v[b][2 * i], v[b][2 * i + 1]);
+#pragma unroll
+  for (int n = 4 * NB; n >= 1; n >>= 1)
+#pragma unroll
+    for (int i = 0; i < n; ++i) t[i] = fmaxf(t[i], t[i + n]);
+  return t[0];
+}
+template <int NB>
+__device__ __forceinline__ float tree_sum(const f32x16 (&v)[NB]) {
+  float t[8 * NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[8 * b + i] = v[b][2 * i] + v[b][2 * i + 1];
+#pragma unroll
+  for (int n = 4 * NB; n >= 1; n >>= 1)
+#pragma unroll
+    for (int i = 0; i < n; ++i) t[i] = t[i] + t[i + n];
+  return t[0];
+}
+
 // Byte-select helpers for the 4x4 bf16 register transpose (v_perm_b32).
 __device__ __forceinline__ uint32_t lo16_pair(uint32_t a, uint32_t b) {  // (a.lo16, b.lo16)
   return __builtin_amdgcn_perm(b, a, 0x05040100u);
@@ -92,6 +121,26 @@ __device__ __forceinline__ void g2lds16(const void* gptr, unsigned char* lds_wav
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------
+// Buffer-resource loads.  One resource per head matrix ([N][D] bf16, at most 16 MiB):
+// the tile offset travels in the scalar soffset operand and each lane's offset inside
+// the tile is loop-invariant, so a tile load costs no VALU address arithmetic.
+// ---------------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr int kBufWord3 = 0x00020000;  // raw (unformatted, unswizzled) dword access
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+// 16 bytes per lane straight into LDS at lds_wave_base + 16*lane
+__device__ __forceinline__ void buf2lds16(buf_rsrc r, uint32_t voff, uint32_t soff, unsigned char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) unsigned char*)lds_wave_base),
+      16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load64(buf_rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// ---------------------------------------------------------------------------------
 // LDS tiles, "blocked chunk-major" layout.
 //
 // A tile is a matrix of R rows, each NCH 16-byte chunks long (8 bf16 per chunk).  The
@@ -118,6 +167,15 @@ template <int NCH>
 __device__ __forceinline__ constexpr uint32_t bcm_byte(uint32_t row, uint32_t ch) {
   return bcm_unit<NCH>(row, ch) * 16;
 }
+// Transposed tiles additionally XOR the in-block row slot with (row / 16) % 4.  The
+// register-path stores write, per instruction, rows d = 4*q + j over many q; without
+// the XOR those rows occupy only 4 of the 16 bank groups (12 conflict cycles per store,
+// measured); with it all 16 are used.  Reads keep 16 consecutive rows of one 16-row
+// block, which the XOR only permutes.
+template <int NCH>
+__device__ __forceinline__ constexpr uint32_t bcm_tr_byte(uint32_t row, uint32_t ch) {
+  return ((row >> 4) * (16 * NCH) + ch * 16 + ((row & 15) ^ ((row >> 4) & 3))) * 16;
+}
 
 // Row of a 32-row block that lane c feeds as the A operand: bits 2 and 3 of c swapped.
 // With it, C register r of lane l belongs to block row 16*(r/8) + 8*(l/32) + (r%8), so
@@ -127,21 +185,31 @@ __device__ __forceinline__ uint32_t row_perm(uint32_t c) { return (c & ~12u) | (
 // Block row held by C register r of a lane in half h (inverse view of row_perm).
 __device__ __forceinline__ constexpr int c_row(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
 
-// Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix into a natural tile.
-// Rows past N are clamped to N-1 (finite data; callers mask them).
+// Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix (buffer resource `r`)
+// into a natural tile.  Rows past N are clamped to N-1 (finite data; callers mask them).
 template <int ROWS, int D, int NWAVES>
-__device__ __forceinline__ void load_nat_tile(const uint16_t* g, int row0, int N, unsigned char* tile, int w, int l) {
+__device__ __forceinline__ void load_nat_tile(buf_rsrc r, int row0, int N, unsigned char* tile, int w, int l) {
   constexpr int NCH = D / 8;
   constexpr int UNITS = ROWS * NCH;
   constexpr int PER_WAVE = UNITS / (NWAVES * 64);
   static_assert(PER_WAVE * NWAVES * 64 == UNITS, "tile must split evenly over the waves");
+  const uint32_t soff = (uint32_t)row0 * (D * 2);
+  if (row0 + ROWS <= N) {  // uniform branch: the common case needs no clamping at all
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int pos = (i * NWAVES + w) * 64 + l;  // unit index written by this lane
-    const int blk = pos / (16 * NCH), rem = pos % (16 * NCH);
-    const int ch = rem >> 4, row = blk * 16 + (rem & 15);
-    const int grow = min(row0 + row, N - 1);
-    g2lds16(g + (size_t)grow * D + ch * 8, tile + (size_t)(i * NWAVES + w) * 64 * 16);
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int pos = (i * NWAVES + w) * 64 + l;  // unit index written by this lane
+      const int blk = pos / (16 * NCH), rem = pos % (16 * NCH);
+      const int ch = rem >> 4, row = blk * 16 + (rem & 15);
+      buf2lds16(r, (uint32_t)(row * (D * 2) + ch * 16), soff, tile + (size_t)(i * NWAVES + w) * 64 * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int pos = (i * NWAVES + w) * 64 + l;
+      const int blk = pos / (16 * NCH), rem = pos % (16 * NCH);
+      const int ch = rem >> 4, row = min(blk * 16 + (rem & 15), N - 1 - row0);
+      buf2lds16(r, (uint32_t)(row * (D * 2) + ch * 16), soff, tile + (size_t)(i * NWAVES + w) * 64 * 16);
+    }
   }
 }
 
@@ -153,16 +221,26 @@ struct TrTile {
   static_assert(NBLK >= 1 && NBLK * NTHREADS == (ROWS / 4) * (D / 4), "tile must split evenly over the threads");
   u32x2 r[NBLK][4];
 
-  __device__ __forceinline__ void fetch(const uint16_t* g, int row0, int N, int tid) {
+  __device__ __forceinline__ void fetch(buf_rsrc rs, int row0, int N, int tid) {
+    const uint32_t soff = (uint32_t)row0 * (D * 2);
+    if (row0 + ROWS <= N) {  // uniform branch: the common case needs no clamping at all
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
-      const int vb = tid + i * NTHREADS;
-      const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
-      const int k0 = kc * 8 + hsel * 4;
+      for (int i = 0; i < NBLK; ++i) {
+        const int vb = tid + i * NTHREADS;
+        const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
+        const int k0 = kc * 8 + hsel * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int grow = min(row0 + k0 + j, N - 1);
-        r[i][j] = *(const u32x2*)(g + (size_t)grow * D + dq * 4);
+        for (int j = 0; j < 4; ++j) r[i][j] = buf_load64(rs, (uint32_t)((k0 + j) * (D * 2) + dq * 8), soff);
+      }
+    } else {
+      const int lim = N - 1 - row0;
+#pragma unroll
+      for (int i = 0; i < NBLK; ++i) {
+        const int vb = tid + i * NTHREADS;
+        const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
+        const int k0 = kc * 8 + hsel * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[i][j] = buf_load64(rs, (uint32_t)(min(k0 + j, lim) * (D * 2) + dq * 8), soff);
       }
     }
   }
@@ -183,7 +261,7 @@ struct TrTile {
           out[0] = lo16_pair(r[i][0][half], r[i][1][half]);
           out[1] = lo16_pair(r[i][2][half], r[i][3][half]);
         }
-        lds_write64(tile, bcm_byte<ROWS / 8>(dq * 4 + j, kc) + hsel * 8, out);
+        lds_write64(tile, bcm_tr_byte<ROWS / 8>(dq * 4 + j, kc) + hsel * 8, out);
       }
     }
   }
@@ -206,7 +284,11 @@ struct TrFrag {
   static constexpr int NCH = R / 8;
   static constexpr uint32_t DB = 2 * 16 * NCH * 16;  // 32 head-dim rows
   static constexpr uint32_t CH = 16 * 16;            // one chunk (8 tile rows)
-  __device__ __forceinline__ static uint32_t base(int c, int h) { return bcm_byte<NCH>(c, h); }
+  // the slot XOR depends on (d / 16) % 4 = (2*db + c/16) % 4, i.e. on the parity of db:
+  // base(c, h, db & 1) + db * DB + (4*rb + 2*sb) * CH
+  __device__ __forceinline__ static uint32_t base(int c, int h, int dbpar) {
+    return bcm_tr_byte<NCH>(c + 32 * dbpar, h) - dbpar * DB;
+  }
 };
 
 // Store a C fragment holding X^T (rows = head-dim d, column = this lane's row `row`)

@@ -18,6 +18,8 @@ int check_shape(int B, int H, int N, int d) {
   if (bh > (1ull << 30)) return FA_ERR_SHAPE;
   const unsigned long long elems = bh * (unsigned long long)N * (unsigned long long)d;
   if (elems >= (1ull << 62)) return FA_ERR_SHAPE;
+  // one head matrix ([N][d] bf16) is addressed through a 32-bit buffer resource
+  if ((unsigned long long)N * (unsigned long long)d * 2ull >= (1ull << 32)) return FA_ERR_SHAPE;
   const unsigned long long qblocks = ((unsigned long long)N + 63) / 64;
   if (qblocks * bh >= (1ull << 31)) return FA_ERR_SHAPE;
   return FA_OK;

@@ -56,8 +56,8 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
   const int b = bh / p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
-  const uint16_t* __restrict__ kg = p.k + head;
-  const uint16_t* __restrict__ vg = p.v + head;
+  const buf_rsrc kg = make_rsrc(p.k + head, (uint32_t)N * D * 2);
+  const buf_rsrc vg = make_rsrc(p.v + head, (uint32_t)N * D * 2);
 
   int kv_end = N;
   if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
   const float sl = p.scale_log2;
   TrTile<BN, D, kDqThreads> kt;
   const uint32_t nfrag = NatFrag<D>::base(c, h);  // K and V tiles, A operands of S^T and dP^T
-  const uint32_t tfrag = TrFrag<BN>::base(c, h);  // K^T tile, A operand of dQ^T
+  const uint32_t tfrag[2] = {TrFrag<BN>::base(c, h, 0), TrFrag<BN>::base(c, h, 1)};  // K^T tile, A operand of dQ^T
 
   load_nat_tile<BN, D, kDqWaves>(kg, 0, N, kbuf(0), w, l);
   load_nat_tile<BN, D, kDqWaves>(vg, 0, N, vbuf(0), w, l);
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const u32x4 a = lds_read128(ktbuf(cur), tfrag + db * TrFrag<BN>::DB + (4 * kb + 2 * sb) * TrFrag<BN>::CH);
+            const u32x4 a = lds_read128(ktbuf(cur), tfrag[db & 1] + db * TrFrag<BN>::DB + (4 * kb + 2 * sb) * TrFrag<BN>::CH);
             dq[db] = mfma32(a, dsk[sb], dq[db]);
           }
       }
@@ -209,8 +209,8 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   const int b = bh / p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
-  const uint16_t* __restrict__ qg = p.q + head;
-  const uint16_t* __restrict__ dog = p.dout + head;
+  const buf_rsrc qg = make_rsrc(p.q + head, (uint32_t)N * D * 2);
+  const buf_rsrc dog = make_rsrc(p.dout + head, (uint32_t)N * D * 2);
   const float* __restrict__ lseg = p.lse + (size_t)bh * N;
   const float* __restrict__ dsg = p.dsum + (size_t)bh * N;
 
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   const float sl = p.scale_log2;
   TrTile<BM, D, kKvThreads> qt, dot;
   const uint32_t nfrag = NatFrag<D>::base(c, h);   // Q and dO tiles, A operands of S and dP
-  const uint32_t tfrag = TrFrag<BM>::base(c, h);   // Q^T and dO^T tiles, A operands of dK^T, dV^T
+  const uint32_t tfrag[2] = {TrFrag<BM>::base(c, h, 0), TrFrag<BM>::base(c, h, 1)};  // Q^T, dO^T tiles: A of dK^T, dV^T
 
   // row statistics of one query tile: raw loads into registers now, converted only when
   // stored (using a loaded value early would wait on every load in flight)
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const uint32_t off = tfrag + db * TrFrag<BM>::DB + (4 * qb + 2 * sb) * TrFrag<BM>::CH;
+            const uint32_t off = tfrag[db & 1] + db * TrFrag<BM>::DB + (4 * qb + 2 * sb) * TrFrag<BM>::CH;
             ao[sb][db] = lds_read128(st + St::DOT, off);
             at[sb][db] = lds_read128(st + St::QT, off);
           }

@@ -15,6 +15,8 @@
 //
 // Work is parallel over query blocks and heads (wiki page, FA2 (2)); each wave owns
 // complete query rows so row statistics never cross waves (FA2 (3)).
+#include <type_traits>
+
 #include "common.hpp"
 #include "fa_kernels.hpp"
 
@@ -26,6 +28,11 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
+// Conditional rescaling threshold in log2 units (FlashAttention-4 summary, second
+// optimisation; wiki page, FA4 (2)): the reference max moves only when a row max grows
+// by more than this, so un-normalised probabilities stay below 2^8.
+constexpr float kRescaleTau = 8.0f;
+constexpr int kLdsTiles = 4;  // 2 K tiles + 2 V^T tiles
 
 template <int D, int BN, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
@@ -34,7 +41,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   constexpr int NKB = BN / 32;            // 32-key blocks per tile
   constexpr int NDB = D / 32;             // 32-row blocks of the head dim
   constexpr int NKK = D / 16;             // k-steps of the QK^T contraction
-  // LDS: K tiles (natural) at [0, 2*TILE_BYTES), V^T tiles at [2*TILE_BYTES, 4*TILE_BYTES)
+  // LDS: 2-deep rings of K tiles (natural) at [0, 2*TILE_BYTES) and of V^T tiles at
+  // [2*TILE_BYTES, 4*TILE_BYTES)
   auto kbuf = [&](int i) { return smem + i * TILE_BYTES; };
   auto vbuf = [&](int i) { return smem + (2 + i) * TILE_BYTES; };
 
@@ -50,8 +58,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
   const uint16_t* __restrict__ qg = p.q + head;
-  const uint16_t* __restrict__ kg = p.k + head;
-  const uint16_t* __restrict__ vg = p.v + head;
+  const buf_rsrc kg = make_rsrc(p.k + head, (uint32_t)N * D * 2);
+  const buf_rsrc vg = make_rsrc(p.v + head, (uint32_t)N * D * 2);
 
   int kv_end = N;
   if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);
@@ -90,102 +98,155 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled-log2 scores
+  float m_run = -INFINITY;  // reference max of scaled-log2 scores (at most kRescaleTau below the true max)
   float l_run = 0.f;        // this lane's partial row sum (the other half-wave holds the rest)
   const float sl = p.scale_log2;
 
   TrTile<BN, D, kThreads> vt;
   const uint32_t kfrag = NatFrag<D>::base(c, h);  // K tile, A operand of S^T
-  const uint32_t vfrag = TrFrag<BN>::base(c, h);  // V^T tile, A operand of O^T
+  const uint32_t vfrag[2] = {TrFrag<BN>::base(c, h, 0), TrFrag<BN>::base(c, h, 1)};  // V^T tile, A operand of O^T
 
-  // ---- prologue: tile 0
-  load_nat_tile<BN, D, kWaves>(kg, 0, N, kbuf(0), w, l);
-  vt.fetch(vg, 0, N, tid);
-  wait_vmem();
-  vt.store(vbuf(0), tid);
-  __syncthreads();
+  // ---- the two operations of the tile pipeline ------------------------------------
+  u32x4 pk[NKB][2];  // P of the tile between its softmax and its P V product
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) {
-      load_nat_tile<BN, D, kWaves>(kg, (t + 1) * BN, N, kbuf(cur ^ 1), w, l);
-      vt.fetch(vg, (t + 1) * BN, N, tid);
+  // MFMA operation for tile j: O += V_j^T P_j (P from the preceding softmax), then the
+  // scores of tile j + 1 into `s`.  The operand fragments stream from LDS with a fixed
+  // look-ahead: fragment i + kLook is requested before MFMA i issues, so each MFMA waits
+  // only for a read issued kLook MFMAs (~kLook * 32 cycles) earlier.
+  constexpr int NPV = NKB * 2 * NDB;  // P V^T MFMAs of one tile
+  constexpr int NS = NKB * NKK;       // Q K^T MFMAs of one tile
+  constexpr int kLook = 4;
+  f32x16 s[NKB];  // scores of the next tile to go through the softmax
+  auto mfma_stream = [&](auto first_c, auto count_c, const unsigned char* vb_, const unsigned char* kt) {
+    constexpr int F = decltype(first_c)::value, M = decltype(count_c)::value;
+    // flat MFMA index i: [0, NPV) = P V^T (kb, sb, db), [NPV, NPV+NS) = Q K^T (kk, kb)
+    auto read_frag = [&](int i) -> u32x4 {
+      if (i < NPV) {
+        const int kb = i / (2 * NDB), sb = (i / NDB) % 2, db = i % NDB;
+        return lds_read128(vb_, vfrag[db & 1] + db * TrFrag<BN>::DB + (4 * kb + 2 * sb) * TrFrag<BN>::CH);
+      }
+      const int kk = (i - NPV) / NKB, kb = (i - NPV) % NKB;
+      return lds_read128(kt, kfrag + kb * NatFrag<D>::BLK + kk * NatFrag<D>::KK);
+    };
+    u32x4 fr[kLook];
+#pragma unroll
+    for (int i = 0; i < kLook && i < M; ++i) fr[i] = read_frag(F + i);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const u32x4 a = fr[i % kLook];
+      if (i + kLook < M) fr[i % kLook] = read_frag(F + i + kLook);
+      __builtin_amdgcn_sched_barrier(0);
+      const int fi = F + i;
+      if (fi < NPV) {
+        const int kb = fi / (2 * NDB), sb = (fi / NDB) % 2, db = fi % NDB;
+        o[db] = mfma32(a, pk[kb][sb], o[db]);
+      } else {
+        // kb fastest: the NKB accumulation chains alternate, so no MFMA waits on the
+        // result of the one issued just before it
+        const int kk = (fi - NPV) / NKB, kb = (fi - NPV) % NKB;
+        s[kb] = mfma32(a, qf[kk], kk == 0 ? f32x16{} : s[kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const int kt0 = t * BN;
-    if (kt0 < wave_kend) {
-      // ---- S^T = K Q^T for the BN keys of this tile
-      f32x16 s[NKB];
-      const unsigned char* kb_ = kbuf(cur);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 a = lds_read128(kb_, kfrag + kb * NatFrag<D>::BLK + kk * NatFrag<D>::KK);
-          s[kb] = mfma32(a, qf[kk], s[kb]);
-        }
-      }
-      // ---- mask (edge tiles only)
-      bool need_mask = kt0 + BN > kv_end;
-      if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > q0 + w * kRowsPerWave);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + 32 * kb + c_row(r, h);
-            bool bad = key >= kv_end;
-            if constexpr (CAUSAL) bad = bad || key > qrow;
-            if (bad) s[kb][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax (scaled-log2 units)
-      float mx = -INFINITY;
+  };
+  auto op_mfma = [&](int j) {  // j = -1: scores of tile 0 only
+    const bool do_pv = j >= 0 && j < ntiles && j * BN < wave_kend;
+    const int jn = j + 1;
+    const bool do_s = jn < ntiles && jn * BN < wave_kend;
+    const unsigned char* vb_ = vbuf(j & 1);
+    const unsigned char* kt = kbuf(jn & 1);
+    if (do_pv && do_s) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV + NS>{}, vb_, kt);
+    else if (do_pv) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV>{}, vb_, kt);
+    else if (do_s) mfma_stream(std::integral_constant<int, NPV>{}, std::integral_constant<int, NS>{}, vb_, kt);
+  };
+
+  // VALU operation for tile j: mask, online softmax with conditional rescaling, P -> pk.
+  auto op_softmax = [&](int j) {
+    const int kt0 = j * BN;
+    if (j >= ntiles || kt0 >= wave_kend) return;
+    bool need_mask = kt0 + BN > kv_end;
+    if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > q0 + w * kRowsPerWave);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx * sl);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + 32 * kb + c_row(r, h);
+          bool bad = key >= kv_end;
+          if constexpr (CAUSAL) bad = bad || key > qrow;
+          s[kb][r] = bad ? -INFINITY : s[kb][r];
+        }
+    }
+    // row max and row sum are reduced as trees: in this phase the wave has the VALU to
+    // itself, so a serial 32-long dependency chain would leave it idle between issues
+    float mx = tree_max<NKB>(s);
+    mx = half_max(mx) * sl;
+    // The reference max only moves when some row of the wave grew by more than tau:
+    // results are exact for any reference (it cancels in O and is added back in the
+    // LSE); tau bounds the un-normalised P by 2^tau.
+    if (__any(mx > m_run + kRescaleTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      u32x4 pk[NKB][2];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * sb + 2 * i], sl, -m_use));
-            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * sb + 2 * i + 1], sl, -m_use));
-            // the row sum uses the unrounded fp32 P: the log-sum-exp the backward
-            // recomputes P from must be accurate to fp32, not to bf16
-            l_run += p0 + p1;
-            pk[kb][sb][i] = pack_bf16x2(p0, p1);
-          }
-      // ---- O^T += V^T P^T
-      const unsigned char* vb_ = vbuf(cur);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const u32x4 a = lds_read128(vb_, vfrag + db * TrFrag<BN>::DB + (4 * kb + 2 * sb) * TrFrag<BN>::CH);
-            o[db] = mfma32(a, pk[kb][sb], o[db]);
-          }
-        }
     }
-    if (has_next) {
-      wait_vmem();
-      vt.store(vbuf(cur ^ 1), tid);
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], sl, -m_use));
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[kb][sb][i] = pack_bf16x2(s[kb][8 * sb + 2 * i], s[kb][8 * sb + 2 * i + 1]);
+    // the row sum uses the unrounded fp32 P: the log-sum-exp the backward recomputes P
+    // from must be accurate to fp32, not to bf16
+    l_run += tree_sum<NKB>(s);
+  };
+
+  // ---- phase schedule ---------------------------------------------------------------
+  // Every wave runs  [S_0] softmax_0 [PV_0,S_1] softmax_1 [PV_1,S_2] ...  Waves 0-3
+  // (group 0) and 4-7 (group 1) hold one wave per SIMD each and run this sequence one
+  // phase apart, so in every phase one wave of each SIMD issues MFMAs while the other
+  // runs the softmax on the VALU.  Each phase ends with a workgroup barrier.  Tile
+  // loads: even phase 2j issues K_{j+1} and V_j (register staged); odd phase 2j+1 stores
+  // V_j^T before its barrier.  MFMA operation j (PV_j, S_{j+1}) runs in phases 2j+2 and
+  // 2j+3, so both rings are two deep: a buffer is refilled only after both groups used it.
+  const int grp = w >> 2;
+  auto begin_phase = [&](int ph) {
+    if (ph & 1) return;
+    const int j = ph >> 1;
+    if (j + 1 < ntiles) load_nat_tile<BN, D, kWaves>(kg, (j + 1) * BN, N, kbuf((j + 1) & 1), w, l);
+    if (j < ntiles) vt.fetch(vg, j * BN, N, tid);
+  };
+  auto end_phase = [&](int ph) {
+    if (ph & 1) {
+      const int j = ph >> 1;
+      if (j < ntiles) {
+        wait_vmem();
+        vt.store(vbuf(j & 1), tid);
+      }
     }
     __syncthreads();
+  };
+
+  load_nat_tile<BN, D, kWaves>(kg, 0, N, kbuf(0), w, l);
+  wait_vmem();
+  __syncthreads();
+  // operation index of group 0 in phase ph is ph, of group 1 is ph - 1:
+  //   op 0 = S_0, op 2j+1 = softmax_j, op 2j+2 = (PV_j, S_{j+1})
+  for (int ph = 0; ph < 2 * ntiles + 2; ++ph) {
+    begin_phase(ph);
+    const int op = ph - grp;
+    if (op >= 0) {
+      if (op & 1) op_softmax(op >> 1);
+      else op_mfma((op >> 1) - 1);
+    }
+    end_phase(ph);
   }
 
   // ---- epilogue: normalise once, store O and LSE
@@ -200,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
 
 template <int D, int BN, bool CAUSAL, bool KVLEN>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-  constexpr size_t lds = 4ull * BN * D * 2;
+  constexpr size_t lds = kLdsTiles * BN * D * 2;
   auto kern = fa_fwd_kernel<D, BN, CAUSAL, KVLEN>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

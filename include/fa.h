@@ -28,7 +28,7 @@
  *    and keys).  Both masks may be combined.
  *  - scale must be finite and > 0 (it multiplies Q K^T before the softmax).
  *  - Supported head dims: d = 64 and d = 128.  Any N >= 1, B >= 1, H >= 1 with
- *    B*H*N*d < 2^62.
+ *    B*H*N*d < 2^62 and N*d*2 < 2^32 (one head's matrix below 4 GiB).
  *  - The caller owns every buffer.  The library never allocates, frees or
  *    synchronises; it only enqueues kernels on `stream` (0 = the null stream) and
  *    returns.  Execution faults surface at the caller's next synchronisation.
