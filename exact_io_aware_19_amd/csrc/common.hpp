@@ -4,17 +4,32 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa355 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded in
+// the source (no reliance on the unroller, whose size limits long schedules exceed).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---------------------------------------------------------------------------------
 // MFMA 32x32x16 bf16 -> fp32.  Fragment layout (checked on gfx950 with a probe):
@@ -290,6 +305,70 @@ struct TrFrag {
     return bcm_tr_byte<NCH>(c + 32 * dbpar, h) - dbpar * DB;
   }
 };
+
+// ---------------------------------------------------------------------------------
+// Swizzled tiles.  The blocked chunk-major arrangement above with the in-block row slot
+// XORed by (ch % 4) | ((row / 16) % 2) << 2:
+//     unit(r, ch) = (r/16)*16*NCH + ch*16 + ((r%16) ^ ((ch%4) | ((r/16)%2) << 2))
+// The XOR keeps MFMA operand reads conflict-free (16 lanes read the 16 rows of one
+// block at one chunk; the XOR only permutes the slots) and also makes the 8x8 block
+// transposition below conflict-free: its 16-lane phases read 16 blocks whose
+// (row-block % 4, chunk % 4) pairs are all different, and write likewise.
+// Within 8 consecutive rows 8a .. 8a+7 of one chunk the slot is (8a%16) + (j ^ x) for
+// a lane-constant x < 8, so the byte address of row 8a + j is addr(8a) ^ (16 j).
+// ---------------------------------------------------------------------------------
+template <int NCH>
+__device__ __forceinline__ constexpr uint32_t swz_unit(uint32_t row, uint32_t ch) {
+  return (row >> 4) * (16 * NCH) + ch * 16 + ((row & 15) ^ ((ch & 3) | (((row >> 4) & 1) << 2)));
+}
+
+// Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix into a swizzled tile,
+// one wave instruction (1 KB) at a time: instruction ii of wave w fills the 64
+// consecutive 16-byte units starting at unit 64*(ii*NWAVES + w); the lane filling unit
+// u fetches the (row, chunk) that the swizzle places there.  Rows past N are clamped to
+// N-1 (finite data; callers give them zero weight).
+template <int ROWS, int D, int NWAVES>
+struct SwzCopy {
+  static constexpr int NCH = D / 8;
+  static constexpr int PER_WAVE = ROWS * NCH / (NWAVES * 64);  // instructions per wave
+  static_assert(PER_WAVE * NWAVES * 64 == ROWS * NCH, "tile must split evenly over the waves");
+  __device__ __forceinline__ static void issue(buf_rsrc r, int row0, int N, unsigned char* tile, int w, int l,
+                                               int ii) {
+    const int u = (ii * NWAVES + w) * 64 + l;
+    const int blk = u / (16 * NCH), ch = (u % (16 * NCH)) >> 4, slot = u & 15;
+    const int row = min(blk * 16 + (slot ^ ((ch & 3) | ((blk & 1) << 2))), N - 1 - row0);
+    buf2lds16(r, (uint32_t)(row * (D * 2) + ch * 16), (uint32_t)row0 * (D * 2),
+              tile + (size_t)(ii * NWAVES + w) * 64 * 16);
+  }
+};
+
+// 4 bytes per lane straight into LDS at lds_wave_base + 4*lane.
+__device__ __forceinline__ void g2lds4(const void* gptr, unsigned char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void*)gptr,
+                                   (__attribute__((address_space(3))) void*)(
+                                       (__attribute__((address_space(3))) unsigned char*)lds_wave_base),
+                                   4, 0, 0);
+}
+
+// Transposition of one 8x8 bf16 block between swizzled tiles: rows 8*rc .. 8*rc+7,
+// chunk dc of a natural [R][D] tile become rows 8*dc .. 8*dc+7, chunk rc of the
+// transposed [D][R] tile.  rd = byte address of (row 8*rc, chunk dc) in the natural tile,
+// wr = byte address of (row 8*dc, chunk rc) in the transposed one.
+__device__ __forceinline__ void transpose8x8(const unsigned char* nat, uint32_t rd, unsigned char* tr, uint32_t wr) {
+  u32x4 x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = lds_read128(nat, rd ^ (16u * j));
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    // output row jj holds element jj of the 8 input rows; dword p = rows 2p, 2p+1
+    u32x4 y;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      y[p] = (jj & 1) ? hi16_pair(x[2 * p][jj >> 1], x[2 * p + 1][jj >> 1])
+                      : lo16_pair(x[2 * p][jj >> 1], x[2 * p + 1][jj >> 1]);
+    lds_write128(tr, wr ^ (16u * jj), y);
+  }
+}
 
 // Store a C fragment holding X^T (rows = head-dim d, column = this lane's row `row`)
 // as bf16 row `row` of a [N][D] matrix, scaled by `mul`.

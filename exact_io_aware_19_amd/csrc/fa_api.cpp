@@ -53,10 +53,13 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   return fa355::launch_forward(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Rows per head in the backward workspace: N rounded up to the dQ pass's 256-row blocks.
+int workspace_rows(int N) { return (N + 255) / 256 * 256; }
+
 size_t workspace_bytes(int B, int H, int N, int d) {
   (void)d;
-  const size_t rows = (size_t)B * H * N;
-  return (rows * 4 + 255) & ~(size_t)255;  // D_i = rowsum(dO * O), fp32 [B][H][N]
+  // D_i and LSE_i * log2(e), fp32 [B][H][nw] each
+  return 2 * (size_t)B * H * workspace_rows(N) * 4;
 }
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -82,7 +85,9 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
   a.kv_len = kv_len;
-  a.dsum = (float*)workspace;
+  a.nw = workspace_rows(N);
+  a.ws_d = (float*)workspace;
+  a.ws_l = (float*)workspace + (size_t)B * H * a.nw;
   a.B = B;
   a.H = H;
   a.N = N;

@@ -23,6 +23,8 @@
 //   launch 2  fa_bwd_dkdv_kernel  (key-outer, 4 waves x 32 key columns)
 //             S = Q K^T, dP = dO V^T, dS = P * (dP - D);
 //             dV^T += dO^T P,  dK^T += Q^T dS
+#include <type_traits>
+
 #include "common.hpp"
 #include "fa_kernels.hpp"
 
@@ -90,11 +92,15 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
     }
     di = row_ok ? half_sum(di) : 0.f;
   }
-  if (row_ok && h == 0) p.dsum[(size_t)bh * N + qrow] = di;
   float lse2 = INFINITY;  // P = exp2(s * scale * log2e - lse2); +inf gives P = 0
   if (row_ok) {
     const float ln = p.lse[(size_t)bh * N + qrow];
     lse2 = (ln == -INFINITY) ? INFINITY : ln * kLog2e;
+  }
+  // row statistics for the dK/dV pass; the grid covers exactly the nw padded rows
+  if (h == 0) {
+    p.ws_d[(size_t)bh * p.nw + qrow] = di;
+    p.ws_l[(size_t)bh * p.nw + qrow] = lse2;
   }
 
   f32x16 dq[NDB];
@@ -180,26 +186,49 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
 
 // --------------------------------------------------------------------------------------
 // launch 2: dK, dV
+//
+// One workgroup = 4 waves x 32 key columns; each wave keeps its keys' K and V fragments
+// and its dK^T, dV^T accumulators in registers and streams the query tiles (BM rows).
+// Per query tile the workgroup fetches Q and dO once, by direct global->LDS copies into
+// swizzled natural tiles, and builds the transposed tiles Q^T, dO^T (A operands of dK^T
+// and dV^T) from them in LDS with 8x8 register transpositions.  The per-row statistics
+// (LSE * log2 e and D) come from the dQ pass's workspace, also by direct copies.
+//
+// Software pipeline over query tiles: while tile i is reduced into dK^T, dV^T, the
+// scores of tile i+1 (S, dP and from them P, dS in bf16) are computed, and tile i+2 is
+// being fetched.  Inside an iteration the 32-query blocks are staggered so that the
+// elementwise work on the scores of one block runs between the dK^T, dV^T products of
+// the previous tile's block:
+//   step q:  S, dP (i+1, q)  then  dV^T, dK^T (i, q)  alongside  P, dS (i+1, q)
+// LDS: 2 x {Q, dO} natural, 2 x {Q^T, dO^T}, 2 x {lse2, D}.
 // --------------------------------------------------------------------------------------
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kKvBN = kKvWaves * 32;  // key columns per workgroup
 
 template <int D, int BM>
-struct KvStage {
-  static constexpr int TILE_BYTES = BM * D * 2;
-  // Q natural, dO natural, Q^T, dO^T, then lse2[BM] and D[BM] (fp32)
-  static constexpr int Q = 0, DO = TILE_BYTES, QT = 2 * TILE_BYTES, DOT = 3 * TILE_BYTES;
-  static constexpr int LSE = 4 * TILE_BYTES, DSUM = 4 * TILE_BYTES + BM * 4;
-  static constexpr int BYTES = 4 * TILE_BYTES + 2 * BM * 4;
+struct KvLds {
+  static constexpr int TILE = BM * D * 2;
+  static constexpr int NAT = 0;         // slot s: Q at NAT + 2*s*TILE, dO right after
+  static constexpr int TR = 4 * TILE;   // slot s: Q^T at TR + 2*s*TILE, dO^T right after
+  static constexpr int ST = 8 * TILE;   // slot s: lse2[BM] at ST + 8*s*BM, D[BM] right after
+  static constexpr int BYTES = 8 * TILE + 2 * 8 * BM;
 };
 
 template <int D, int BM, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  using St = KvStage<D, BM>;
+  using L = KvLds<D, BM>;
+  constexpr int NCH = D / 8, NCHT = BM / 8;
   constexpr int NQB = BM / 32, NDB = D / 32, NKK = D / 16;
-  auto stage = [&](int i) { return smem + i * St::BYTES; };
+  constexpr uint32_t NAT_QB = 32 * NCH * 16;  // bytes per 32 rows of a natural tile
+  constexpr uint32_t TR_DB = 32 * NCHT * 16;  // bytes per 32 rows of a transposed tile
+  auto nat_q = [&](int s) { return smem + L::NAT + 2 * s * L::TILE; };
+  auto nat_d = [&](int s) { return smem + L::NAT + 2 * s * L::TILE + L::TILE; };
+  auto tr_q = [&](int s) { return smem + L::TR + 2 * s * L::TILE; };
+  auto tr_d = [&](int s) { return smem + L::TR + 2 * s * L::TILE + L::TILE; };
+  auto st_l = [&](int s) { return smem + L::ST + 8 * s * BM; };
+  auto st_d = [&](int s) { return smem + L::ST + 8 * s * BM + 4 * BM; };
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
@@ -211,8 +240,8 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   const size_t head = (size_t)bh * N * D;
   const buf_rsrc qg = make_rsrc(p.q + head, (uint32_t)N * D * 2);
   const buf_rsrc dog = make_rsrc(p.dout + head, (uint32_t)N * D * 2);
-  const float* __restrict__ lseg = p.lse + (size_t)bh * N;
-  const float* __restrict__ dsg = p.dsum + (size_t)bh * N;
+  const float* __restrict__ wl = p.ws_l + (size_t)bh * p.nw;
+  const float* __restrict__ wd = p.ws_d + (size_t)bh * p.nw;
 
   int kv_end = N;
   if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);
@@ -236,7 +265,7 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     return;
   }
 
-  // ---- this lane's key column: K and V fragments (B operands)
+  // ---- this lane's key column: K and V fragments (B operands of S and dP)
   u32x4 kf[NKK], vf[NKK];
   {
     const size_t off = head + (size_t)min(kcol, N - 1) * D + 8 * h;
@@ -250,134 +279,211 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   const int i_first = CAUSAL ? (k0 / BM) : 0;
   const int i_last = (N + BM - 1) / BM;  // exclusive
   const float sl = p.scale_log2;
-  TrTile<BM, D, kKvThreads> qt, dot;
-  const uint32_t nfrag = NatFrag<D>::base(c, h);   // Q and dO tiles, A operands of S and dP
-  const uint32_t tfrag[2] = {TrFrag<BM>::base(c, h, 0), TrFrag<BM>::base(c, h, 1)};  // Q^T, dO^T tiles: A of dK^T, dV^T
 
-  // row statistics of one query tile: raw loads into registers now, converted only when
-  // stored (using a loaded value early would wait on every load in flight)
-  float st_lse = 0.f, st_d = 0.f;
-  auto fetch_stats = [&](int i0) {
-    if (tid < BM) {
-      const int q = min(i0 + tid, N - 1);
-      st_lse = lseg[q];
-      st_d = dsg[q];
-    }
-  };
-  auto store_stats = [&](unsigned char* st, int i0) {
-    if (tid < BM) {
-      // lse2 = +inf (P = 0) for rows past N and for rows with no admissible key
-      const bool live = i0 + tid < N && st_lse != -INFINITY;
-      ((float*)(st + St::LSE))[tid] = live ? st_lse * kLog2e : INFINITY;
-      ((float*)(st + St::DSUM))[tid] = live ? st_d : 0.f;
-    }
-  };
-  auto issue = [&](int i, unsigned char* st) {
-    const int i0 = i * BM;
-    load_nat_tile<BM, D, kKvWaves>(qg, i0, N, st + St::Q, w, l);
-    load_nat_tile<BM, D, kKvWaves>(dog, i0, N, st + St::DO, w, l);
-    qt.fetch(qg, i0, N, tid);
-    dot.fetch(dog, i0, N, tid);
-    fetch_stats(i0);
-  };
-  auto finish = [&](unsigned char* st, int i) {
-    wait_vmem();
-    qt.store(st + St::QT, tid);
-    dot.store(st + St::DOT, tid);
-    store_stats(st, i * BM);
-  };
-
-  issue(i_first, stage(0));
-  finish(stage(0), i_first);
-  __syncthreads();
-
-  for (int i = i_first; i < i_last; ++i) {
-    const int cur = (i - i_first) & 1;
-    const bool has_next = i + 1 < i_last;
-    if (has_next) issue(i + 1, stage(cur ^ 1));
-    const int i0 = i * BM;
-    unsigned char* st = stage(cur);
-    // causal: skip tiles whose queries all precede this wave's first key
-    if (!CAUSAL || i0 + BM - 1 >= kw0) {
-      const int qoff0 = i0 + 8 * h - kcol;  // (query - key) of this lane's first row
-      // Software pipeline over the 32-query blocks of the tile: the operand reads of
-      // the next phase are issued before the math of the current one, so LDS latency
-      // hides behind MFMA and VALU work of the same wave (one wave per SIMD here).
-      u32x4 aq[NKK], ad[NKK];
+  // Fragment bases.  Natural tiles: lane (c, h) reads row 32*qb + row_perm(c), chunk
+  // 2*kk + h; the swizzle depends on kk only through kk % 2.  Transposed tiles: lane
+  // reads row 32*db + c, chunk 4*qb + 2*sb + h; the swizzle depends on sb.
+  const uint32_t rp = row_perm(c);
+  uint32_t nb[2], tb[2];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        aq[kk] = lds_read128(st + St::Q, nfrag + kk * NatFrag<D>::KK);
-        ad[kk] = lds_read128(st + St::DO, nfrag + kk * NatFrag<D>::KK);
-      }
+  for (int x = 0; x < 2; ++x) {
+    nb[x] = 16 * swz_unit<NCH>(rp, 2 * x + h);
+    tb[x] = 16 * swz_unit<NCHT>(c, 2 * x + h);
+  }
+  // This thread's 8x8 block of the transposition: matrix (waves 0-1 Q, 2-3 dO), row
+  // block rc, chunk dc.  The low four lane bits run over (dc % 4, rc % 4).
+  constexpr int NDC4 = NCH / 4;
+  const int hi = (l >> 4) + 4 * (w & 1);
+  const int tdc = (l & 3) + 4 * (hi % NDC4), trc = ((l >> 2) & 3) + 4 * (hi / NDC4);
+  const uint32_t t_rd = 16 * swz_unit<NCH>(8 * trc, tdc), t_wr = 16 * swz_unit<NCHT>(8 * tdc, trc);
+  const bool t_dO = w >= 2;
+
+  // Direct copies of tile `it` into slot s: item k < 2*PER_WAVE is one 1 KB wave
+  // instruction of Q (k < PER_WAVE) or dO; item 2*PER_WAVE the row statistics (lse2 on
+  // even waves, D on odd ones; with BM = 64 waves 2-3 repeat what 0-1 copy).
+  using Copy = SwzCopy<BM, D, kKvWaves>;
+  constexpr int PER_WAVE = Copy::PER_WAVE;
+  constexpr int NDMA = 2 * PER_WAVE + 1;
+  auto dma_item = [&](int k, int it, int s) {
+    const int i0 = it * BM;
+    if (k < PER_WAVE) {
+      Copy::issue(qg, i0, N, nat_q(s), w, l, k);
+    } else if (k < 2 * PER_WAVE) {
+      Copy::issue(dog, i0, N, nat_d(s), w, l, k - PER_WAVE);
+    } else {
+      constexpr int SW = BM / 64;  // wave instructions per statistic
+      const int which = (w / SW) & 1, part = w % SW, row = i0 + part * 64 + l;
+      g2lds4((which ? wd : wl) + row, (which ? st_d(s) : st_l(s)) + part * 256);
+    }
+  };
+  auto issue = [&](int it, int s) {
+#pragma unroll
+    for (int k = 0; k < NDMA; ++k) dma_item(k, it, s);
+  };
+  // tile `it` needs the causal mask for this wave iff some query precedes some key
+  auto masked = [&](int it) { return CAUSAL && it * BM < kw0 + 31; };
+  // P = exp2(S * scale * log2e - lse2) and dS = P * (dP - D) for two query rows
+  // (C registers r0, r0 + 1 of sc/dp; `qoff` = first row minus this lane's key)
+  // returns (P pair, dS pair) as packed bf16
+  auto prob_pair = [&](auto MASK, const f32x16& sc, const f32x16& dp, int r0, f32x2 l2, f32x2 dd,
+                       int qoff) -> u32x2 {
+    float p0 = fast_exp2(__builtin_fmaf(sc[r0], sl, -l2[0]));
+    float p1 = fast_exp2(__builtin_fmaf(sc[r0 + 1], sl, -l2[1]));
+    if constexpr (decltype(MASK)::value) {  // key kcol is admissible for query q iff kcol <= q
+      p0 = (qoff < 0) ? 0.f : p0;
+      p1 = (qoff + 1 < 0) ? 0.f : p1;
+    }
+    return u32x2{pack_bf16x2(p0, p1), pack_bf16x2(p0 * (dp[r0] - dd[0]), p1 * (dp[r0 + 1] - dd[1]))};
+  };
+  auto stat_pair = [&](const unsigned char* st, int row) {
+    return __builtin_bit_cast(f32x2, *(const __attribute__((address_space(3))) u32x2*)(
+                                          (const __attribute__((address_space(3))) unsigned char*)st + row * 4));
+  };
+
+  // P, dS of the tile being reduced
+  u32x4 pc[NQB][2], dsc[NQB][2];
+
+  // ---- prologue: fetch tiles i_first and i_first+1, transpose and score i_first
+  issue(i_first, 0);
+  issue(min(i_first + 1, i_last - 1), 1);
+  wait_vmem();
+  __syncthreads();
+  transpose8x8(t_dO ? nat_d(0) : nat_q(0), t_rd, t_dO ? tr_d(0) : tr_q(0), t_wr);
+  {
+    auto pro = [&](auto MASK) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          s = mfma32(aq[kk], kf[kk], s);
-          dp = mfma32(ad[kk], vf[kk], dp);
+          const uint32_t off = nb[kk & 1] + qb * NAT_QB + (kk >> 1) * 64 * 16;
+          sc = mfma32(lds_read128(nat_q(0), off), kf[kk], sc);
+          dp = mfma32(lds_read128(nat_d(0), off), vf[kk], dp);
         }
-        // operands of dV^T / dK^T for this block, and statistics of its rows
-        u32x4 ao[2][NDB], at[2][NDB];
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const uint32_t off = tfrag[db & 1] + db * TrFrag<BM>::DB + (4 * qb + 2 * sb) * TrFrag<BM>::CH;
-            ao[sb][db] = lds_read128(st + St::DOT, off);
-            at[sb][db] = lds_read128(st + St::QT, off);
-          }
-        f32x4 lsv[2][2], dsv[2][2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          // the 8 query rows 32*qb + 16*sb + 8*h + 0..7 held by this lane
-          const int rbase = 32 * qb + 16 * sb + 8 * h;
-          lsv[sb][0] = *(const f32x4*)(st + St::LSE + rbase * 4);
-          lsv[sb][1] = *(const f32x4*)(st + St::LSE + rbase * 4 + 16);
-          dsv[sb][0] = *(const f32x4*)(st + St::DSUM + rbase * 4);
-          dsv[sb][1] = *(const f32x4*)(st + St::DSUM + rbase * 4 + 16);
+        for (int u = 0; u < 8; ++u) {
+          const int sb = u >> 2, e = u & 3, row = 32 * qb + 16 * sb + 8 * h + 2 * e;
+          const u32x2 pd = prob_pair(MASK, sc, dp, 8 * sb + 2 * e, stat_pair(st_l(0), row),
+                                     stat_pair(st_d(0), row), i_first * BM + row - kcol);
+          pc[qb][sb][e] = pd[0];
+          dsc[qb][sb][e] = pd[1];
         }
-        // next block's S/dP operands
-        if (qb + 1 < NQB) {
-#pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) {
-            aq[kk] = lds_read128(st + St::Q, nfrag + (qb + 1) * NatFrag<D>::BLK + kk * NatFrag<D>::KK);
-            ad[kk] = lds_read128(st + St::DO, nfrag + (qb + 1) * NatFrag<D>::BLK + kk * NatFrag<D>::KK);
-          }
-        }
-        // P = exp2(S * scale * log2e - LSE * log2e), dS = P * (dP - D)
-        u32x4 pk[2], dsk[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r0 = 8 * sb + 2 * e;
-            const float l0 = lsv[sb][e >> 1][(2 * e) & 3], l1 = lsv[sb][e >> 1][(2 * e + 1) & 3];
-            const float d0 = dsv[sb][e >> 1][(2 * e) & 3], d1 = dsv[sb][e >> 1][(2 * e + 1) & 3];
-            float p0 = fast_exp2(__builtin_fmaf(s[r0], sl, -l0));
-            float p1 = fast_exp2(__builtin_fmaf(s[r0 + 1], sl, -l1));
-            if constexpr (CAUSAL) {
-              // key kcol is admissible for query q iff kcol <= q; qoff = q - kcol
-              const int qoff = qoff0 + 32 * qb + 16 * sb + 2 * e;
-              p0 = (qoff < 0) ? 0.f : p0;
-              p1 = (qoff + 1 < 0) ? 0.f : p1;
-            }
-            pk[sb][e] = pack_bf16x2(p0, p1);
-            dsk[sb][e] = pack_bf16x2(p0 * (dp[r0] - d0), p1 * (dp[r0 + 1] - d1));
-          }
-        // dV^T += dO^T P,  dK^T += Q^T dS
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dv[db] = mfma32(ao[sb][db], pk[sb], dv[db]);
-            dk[db] = mfma32(at[sb][db], dsk[sb], dk[db]);
-          }
       }
-    }
-    if (has_next) finish(stage(cur ^ 1), i + 1);
+    };
+    if (masked(i_first)) pro(std::true_type{});
+    else pro(std::false_type{});
+  }
+  __syncthreads();
+
+  // ---- steady state.  Iteration i: reduce tile i (slot cs) while scoring tile i+1
+  // (slot ns), transpose tile i+1 and fetch tile i+2 into slot cs.  One flat, fully
+  // unrolled stream of products per iteration; operand fragments are read kLook
+  // products ahead, and the other work is slotted between products (the order is
+  // pinned with scheduling barriers):
+  //   per 32-query block q:  NS products S, dP (i+1, q), then NR products dV^T, dK^T
+  //   (i, q) with the eight P, dS pair groups of (i+1, q) between them;
+  //   products 0-7 carry the transposition reads, 8-15 its permutes and writes, and
+  //   every fourth product from 16 on one direct copy of tile i+2.
+  constexpr int NS = 2 * NKK, NR = 4 * NDB, NSTEP = NS + NR, T = NQB * NSTEP;
+  constexpr int UNIT_OPS = NR / 8;  // reduce products per P, dS group
+  constexpr int kLook = 4;
+  static_assert(UNIT_OPS >= 1 && 8 * UNIT_OPS == NR, "eight P, dS groups per block");
+  static_assert(16 + 4 * NDMA <= T, "copies must fit in the stream");
+  auto iteration = [&](auto MASK, int i) {
+    const int cs = (i - i_first) & 1, ns = cs ^ 1;
+    const int it = i + 1, it2 = min(i + 2, i_last - 1);  // past the end: refetch, unused
+    const unsigned char* t_src = t_dO ? nat_d(ns) : nat_q(ns);
+    unsigned char* t_dst = t_dO ? tr_d(ns) : tr_q(ns);
+    auto aread = [&](int t) -> u32x4 {
+      const int q = t / NSTEP, r = t % NSTEP;
+      if (r < NS) {
+        const int kk = r >> 1;
+        return lds_read128((r & 1) ? nat_d(ns) : nat_q(ns), nb[kk & 1] + q * NAT_QB + (kk >> 1) * 64 * 16);
+      }
+      const int m = r - NS, sb = m / (2 * NDB), db = (m >> 1) % NDB;
+      return lds_read128((m & 1) ? tr_q(cs) : tr_d(cs), tb[sb] + db * TR_DB + q * 64 * 16);
+    };
+    u32x4 fr[kLook];
+#pragma unroll
+    for (int t = 0; t < kLook; ++t) fr[t] = aread(t);
+    f32x16 sc = f32x16{}, dp = f32x16{};
+    u32x4 pn[NQB][2], dsn[NQB][2];
+    u32x4 tx[8];
+    f32x2 sl2[3], sd2[3];  // statistics of the P, dS groups in flight
+    static_for<T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      constexpr int q = t / NSTEP, r = t % NSTEP;
+      const u32x4 a = fr[t % kLook];
+      if constexpr (t + kLook < T) fr[t % kLook] = aread(t + kLook);
+      if constexpr (t < 8) {
+        tx[t] = lds_read128(t_src, t_rd ^ (16u * t));
+      } else if constexpr (t < 16) {
+        constexpr int jj = t - 8;
+        u32x4 y;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+          y[pp] = (jj & 1) ? hi16_pair(tx[2 * pp][jj >> 1], tx[2 * pp + 1][jj >> 1])
+                           : lo16_pair(tx[2 * pp][jj >> 1], tx[2 * pp + 1][jj >> 1]);
+        lds_write128(t_dst, t_wr ^ (16u * jj), y);
+      }
+      if constexpr (t >= 16 && (t - 16) % 4 == 0 && (t - 16) / 4 < NDMA) dma_item((t - 16) / 4, it2, cs);
+      // statistics of group u are read two products before the group runs
+      static_for<8>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (r == NS + (u + 1) * UNIT_OPS - 1 - 2) {
+          const int row = 32 * q + 16 * (u >> 2) + 8 * h + 2 * (u & 3);
+          sl2[u % 3] = stat_pair(st_l(ns), row);
+          sd2[u % 3] = stat_pair(st_d(ns), row);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (r < NS) {
+        constexpr int kk = r >> 1;
+        if constexpr (r & 1) dp = mfma32(a, vf[kk], kk == 0 ? f32x16{} : dp);
+        else sc = mfma32(a, kf[kk], kk == 0 ? f32x16{} : sc);
+      } else {
+        constexpr int m = r - NS, sb = m / (2 * NDB), db = (m >> 1) % NDB;
+        if constexpr (m & 1) dk[db] = mfma32(a, dsc[q][sb], dk[db]);
+        else dv[db] = mfma32(a, pc[q][sb], dv[db]);
+        if constexpr ((m + 1) % UNIT_OPS == 0) {
+          constexpr int u = m / UNIT_OPS, sb2 = u >> 2, e = u & 3;
+          const int row = 32 * q + 16 * sb2 + 8 * h + 2 * e;
+          const u32x2 pd = prob_pair(MASK, sc, dp, 8 * sb2 + 2 * e, sl2[u % 3], sd2[u % 3], it * BM + row - kcol);
+          pn[q][sb2][e] = pd[0];
+          dsn[q][sb2][e] = pd[1];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        pc[qb][sb] = pn[qb][sb];
+        dsc[qb][sb] = dsn[qb][sb];
+      }
+    wait_vmem();
     __syncthreads();
+  };
+  // The causal mask is needed only on the first tiles (queries before the wave's keys):
+  // masked and unmasked iterations run in two loops of straight-line bodies.  Every
+  // wave passes the same number of barriers, one per iteration.
+  int i = i_first;
+  if constexpr (CAUSAL)
+    for (; i + 1 < i_last && masked(i + 1); ++i) iteration(std::true_type{}, i);
+  for (; i + 1 < i_last; ++i) iteration(std::false_type{}, i);
+  {
+    const int cs = (i - i_first) & 1;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const uint32_t off = tb[sb] + db * TR_DB + qb * 64 * 16;
+          dv[db] = mfma32(lds_read128(tr_d(cs), off), pc[qb][sb], dv[db]);
+          dk[db] = mfma32(lds_read128(tr_q(cs), off), dsc[qb][sb], dk[db]);
+        }
   }
   if (col_store) {
     // keys padded away for every query get exact zeros
@@ -406,7 +512,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   {
-    constexpr size_t lds = 2ull * KvStage<D, BM>::BYTES;
+    constexpr size_t lds = KvLds<D, BM>::BYTES;
     auto kern = fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN>;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;

@@ -74,9 +74,10 @@ int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float
                      float scale, int causal, const int32_t* kv_len, fa_stream_t stream);
 
 /*
- * Size in bytes of the device workspace fa_backward needs: one fp32 per query row for
- * D_i = sum_k dO_ik O_ik (4*B*H*N bytes, rounded up to 256).  dQ needs no accumulator:
- * it is produced by a query-outer pass that keeps its rows in registers.  Returns 0 for
+ * Size in bytes of the device workspace fa_backward needs: two fp32 per query row,
+ * D_i = sum_k dO_ik O_ik and LSE_i * log2(e), for N rounded up to a multiple of 256
+ * rows per head: 8 * B * H * (256 * ceil(N / 256)) bytes.  dQ needs no accumulator: it
+ * is produced by a query-outer pass that keeps its rows in registers.  Returns 0 for
  * invalid sizes.
  */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);

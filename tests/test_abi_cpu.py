@@ -71,8 +71,8 @@ def test_forward_kvlen_rejects(lib):
 
 def test_workspace_size(lib):
     B, H, N, d = 2, 3, 100, 128
-    rows = B * H * N
-    want = ((rows * 4 + 255) // 256) * 256
+    nw = (N + 255) // 256 * 256  # rows per head, padded to the dQ pass's 256-row blocks
+    want = 2 * 4 * B * H * nw  # D_i and LSE_i * log2(e), fp32
     assert lib.fa_backward_workspace_size(B, H, N, d) == want
     assert lib.fa_backward_workspace_size(0, H, N, d) == 0
     assert lib.fa_backward_workspace_size(B, H, N, 72) == 0
