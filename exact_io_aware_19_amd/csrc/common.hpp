@@ -44,6 +44,25 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                  0, 0);
 }
 
+// The same product with the accumulator in ordinary vector registers and B read from
+// accumulation registers, as inline assembly.  The compiler picks one accumulator form
+// per kernel; where it keeps accumulators in accumulation registers, VALU code that
+// reads a product (v_accvgpr_read) while other products run is slow, so products whose
+// results feed VALU code use these.  The compiler does not know these are MFMAs: a VALU
+// read of the result must come at least kMfmaValuWait wait states after the product
+// (callers insert them with mfma_valu_wait()); a following product may accumulate into
+// the result directly.
+constexpr int kMfmaValuWait = 12;  // 32x32x16 bf16 result -> VALU read, gfx950
+__device__ __forceinline__ f32x16 mfma32_vz(const u32x4& a, const u32x4& b_acc) {  // C = 0
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b_acc));
+  return d;
+}
+__device__ __forceinline__ void mfma32_vacc(f32x16& d, const u32x4& a, const u32x4& b_acc) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b_acc));
+}
+__device__ __forceinline__ void mfma_valu_wait() { asm volatile("s_nop 7\n\ts_nop 3" ::: "memory"); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -308,18 +327,20 @@ struct TrFrag {
 
 // ---------------------------------------------------------------------------------
 // Swizzled tiles.  The blocked chunk-major arrangement above with the in-block row slot
-// XORed by (ch % 4) | ((row / 16) % 2) << 2:
-//     unit(r, ch) = (r/16)*16*NCH + ch*16 + ((r%16) ^ ((ch%4) | ((r/16)%2) << 2))
-// The XOR keeps MFMA operand reads conflict-free (16 lanes read the 16 rows of one
-// block at one chunk; the XOR only permutes the slots) and also makes the 8x8 block
-// transposition below conflict-free: its 16-lane phases read 16 blocks whose
-// (row-block % 4, chunk % 4) pairs are all different, and write likewise.
-// Within 8 consecutive rows 8a .. 8a+7 of one chunk the slot is (8a%16) + (j ^ x) for
-// a lane-constant x < 8, so the byte address of row 8a + j is addr(8a) ^ (16 j).
+// XORed by (ch % 4) | 12 * ((row / 16) % 2):
+//     unit(r, ch) = (r/16)*16*NCH + ch*16 + ((r%16) ^ ((ch%4) | 12*((r/16)%2)))
+// Chosen by measurement (SQ_LDS_BANK_CONFLICT on gfx950 for each access pattern): a
+// 128-bit LDS read is served in four 16-lane phases that are not plain lane ranges,
+// and with this XOR the MFMA operand reads (natural and transposed tiles) and the
+// reads and writes of the 8x8 transposition below are all conflict-free; an XOR by 4
+// * ((r/16) % 2) alone, the obvious choice for 16-lane phases 0-15, 16-31, ..., costs
+// a second cycle on every operand read.  Within 8 consecutive rows 8a .. 8a+7 of one
+// chunk the slot is 8*b + (j ^ x) for a lane-constant b, x < 8, so the byte address of
+// row 8a + j is addr(8a) ^ (16 j).
 // ---------------------------------------------------------------------------------
 template <int NCH>
 __device__ __forceinline__ constexpr uint32_t swz_unit(uint32_t row, uint32_t ch) {
-  return (row >> 4) * (16 * NCH) + ch * 16 + ((row & 15) ^ ((ch & 3) | (((row >> 4) & 1) << 2)));
+  return (row >> 4) * (16 * NCH) + ch * 16 + ((row & 15) ^ ((ch & 3) | (((row >> 4) & 1) * 12)));
 }
 
 // Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix into a swizzled tile,
@@ -336,7 +357,7 @@ struct SwzCopy {
                                                int ii) {
     const int u = (ii * NWAVES + w) * 64 + l;
     const int blk = u / (16 * NCH), ch = (u % (16 * NCH)) >> 4, slot = u & 15;
-    const int row = min(blk * 16 + (slot ^ ((ch & 3) | ((blk & 1) << 2))), N - 1 - row0);
+    const int row = min(blk * 16 + (slot ^ ((ch & 3) | ((blk & 1) * 12))), N - 1 - row0);
     buf2lds16(r, (uint32_t)(row * (D * 2) + ch * 16), (uint32_t)row0 * (D * 2),
               tile + (size_t)(ii * NWAVES + w) * 64 * 16);
   }

@@ -215,6 +215,67 @@ struct KvLds {
   static constexpr int BYTES = 8 * TILE + 2 * 8 * BM;
 };
 
+// Compile-time placement of the P, dS groups in the dK/dV stream (see the kernel).  A
+// group runs in three stages on consecutive products (A: S, dP out of the accumulators
+// and the exponent argument; B: exp2 and dP - D; C: products and bf16 packing), so no
+// product slot carries a long dependent chain that would hold back the next product.
+template <int NQB, int NS, int NR>
+struct KvSched {
+  static constexpr int NSTEP = NS + NR, T = NQB * NSTEP;
+  // first stage of group u of block q of the scored tile: groups 0-3 on the block's
+  // dK/dV products, 4-7 on the next block's S/dP products (-1: the last block's groups
+  // 4-7, which run in the next iteration as carried groups of the reduced tile)
+  static constexpr int OFF = NR >= 16 ? 1 : 0;
+  static constexpr int min_(int a, int b) { return a < b ? a : b; }
+  static constexpr int unit_op(int q, int u) {
+    if (u < 4) return min_(q * NSTEP + NS + u * (NR / 4) + OFF, T - 6 + u);
+    if (q + 1 < NQB) return (q + 1) * NSTEP + 1 + (u - 4) * (NS / 4);
+    return -1;
+  }
+  static constexpr int carry_op(int u) { return 1 + (u - 4) * (NS / 4); }  // u = 4..7
+  // group whose first stage runs after op t: 16*q + u for the scored tile, 1000 + u for
+  // a carried group, -1 for none
+  static constexpr int unit_at(int t) {
+    if (t < 0) return -1;
+    for (int u = 4; u < 8; ++u)
+      if (carry_op(u) == t) return 1000 + u;
+    for (int q = 0; q < NQB; ++q)
+      for (int u = 0; u < 8; ++u)
+        if (unit_op(q, u) == t) return 16 * q + u;
+    return -1;
+  }
+  // number of groups starting before op t (ring index of a group's registers)
+  static constexpr int seq(int t) {
+    int n = 0;
+    for (int x = 0; x < t; ++x) n += unit_at(x) >= 0;
+    return n;
+  }
+  // every group starts on its own op and ends inside the iteration; at most three
+  // groups are in flight (ring of three register sets, statistics read two ops ahead)
+  static constexpr bool valid() {
+    int starts[8 * NQB + 4] = {};
+    int n = 0;
+    for (int u = 4; u < 8; ++u) starts[n++] = carry_op(u);
+    for (int q = 0; q < NQB; ++q)
+      for (int u = 0; u < 8; ++u)
+        if (unit_op(q, u) >= 0) starts[n++] = unit_op(q, u);
+    for (int a = 0; a < n; ++a) {
+      if (starts[a] < 0 || starts[a] + 2 >= T) return false;
+      for (int b = 0; b < n; ++b)
+        if (a != b && starts[a] == starts[b]) return false;
+    }
+    for (int a = 1; a < n; ++a)  // sort the starts
+      for (int b = a; b > 0 && starts[b - 1] > starts[b]; --b) {
+        const int x = starts[b];
+        starts[b] = starts[b - 1];
+        starts[b - 1] = x;
+      }
+    for (int k = 0; k + 3 < n; ++k)  // group k+3 reuses the registers of group k
+      if (starts[k + 3] - 2 <= starts[k] + 1) return false;
+    return true;
+  }
+};
+
 template <int D, int BM, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -231,7 +292,8 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   auto st_d = [&](int s) { return smem + L::ST + 8 * s * BM + 4 * BM; };
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
+  // wave index as a scalar: tile copies then compute their LDS destinations in SALU
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 31, h = l >> 5;
   const int BH = p.B * p.H;
   const int kbi = blockIdx.x / BH;  // causal: key block 0 sees the most queries, so it goes first
   const int bh = blockIdx.x % BH;
@@ -291,10 +353,13 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     tb[x] = 16 * swz_unit<NCHT>(c, 2 * x + h);
   }
   // This thread's 8x8 block of the transposition: matrix (waves 0-1 Q, 2-3 dO), row
-  // block rc, chunk dc.  The low four lane bits run over (dc % 4, rc % 4).
+  // block rc, chunk dc.  The low four lane bits run over (dc % 4, rc % 4): lane bits 3
+  // and 0 give dc % 4, bits 1 and 2 give rc % 4 (of the assignments that keep both
+  // the reads and the writes free of bank conflicts, measured on gfx950).
   constexpr int NDC4 = NCH / 4;
   const int hi = (l >> 4) + 4 * (w & 1);
-  const int tdc = (l & 3) + 4 * (hi % NDC4), trc = ((l >> 2) & 3) + 4 * (hi / NDC4);
+  const int tdc = ((l >> 3) & 1) + 2 * (l & 1) + 4 * (hi % NDC4);
+  const int trc = ((l >> 1) & 1) + 2 * ((l >> 2) & 1) + 4 * (hi / NDC4);
   const uint32_t t_rd = 16 * swz_unit<NCH>(8 * trc, tdc), t_wr = 16 * swz_unit<NCHT>(8 * tdc, trc);
   const bool t_dO = w >= 2;
 
@@ -321,27 +386,59 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     for (int k = 0; k < NDMA; ++k) dma_item(k, it, s);
   };
   // tile `it` needs the causal mask for this wave iff some query precedes some key
-  auto masked = [&](int it) { return CAUSAL && it * BM < kw0 + 31; };
   // P = exp2(S * scale * log2e - lse2) and dS = P * (dP - D) for two query rows
   // (C registers r0, r0 + 1 of sc/dp; `qoff` = first row minus this lane's key)
-  // returns (P pair, dS pair) as packed bf16
-  auto prob_pair = [&](auto MASK, const f32x16& sc, const f32x16& dp, int r0, f32x2 l2, f32x2 dd,
-                       int qoff) -> u32x2 {
+  auto stat_pair = [&](const unsigned char* st, int row) {
+    return __builtin_bit_cast(f32x2, *(const __attribute__((address_space(3))) u32x2*)(
+                                          (const __attribute__((address_space(3))) unsigned char*)st + row * 4));
+  };
+
+  // ---- software pipeline --------------------------------------------------------
+  // Iteration i reduces tile i (slot cs) into dK^T, dV^T while it scores tile i+1 (slot
+  // ns), transposes tile i+1 and fetches tile i+2 into slot cs.  It is one flat, fully
+  // unrolled stream of T products whose order is pinned with scheduling barriers:
+  //   block q of 32 queries:  NS products S, dP (i+1, q)  then  NR products dV^T, dK^T (i, q)
+  // with the other work slotted between products:
+  //   - operand fragments are read kLook products ahead;
+  //   - P, dS of (i+1, q) in eight groups of two rows: groups 0-3 ride on the dV^T, dK^T
+  //     products of block q, groups 4-7 on the S, dP products of block q+1 (those of the
+  //     last block on the first block of the next iteration), so that every product
+  //     slot carries about the same amount of VALU work; each group runs in three
+  //     stages on consecutive products (placement in KvSched);
+  //   - the direct copies of tile i+2 (every fourth product from 2: a burst of copies
+  //     stalls instruction issue; early enough that their latency hides behind the
+  //     iteration) and the transposition of tile i+1 (reads
+  //     on products 0-7, one 8-row output on every third product from 8).
+  // P, dS live in two register sets (tile being reduced / tile being scored) whose
+  // roles swap every iteration; iterations run in pairs so the set index is a
+  // compile-time constant and no register copies are needed.  S, dP are double
+  // buffered by block parity.
+  constexpr int NS = 2 * NKK, NR = 4 * NDB, NSTEP = NS + NR, T = NQB * NSTEP;
+  constexpr int kLook = 4;
+  static_assert(NQB % 2 == 0, "S, dP buffers alternate by block parity");
+  static_assert(8 + 3 * 7 < T && 2 + 4 * (NDMA - 1) < T, "extra work must fit in the stream");
+  u32x4 ps[2][NQB][2], dss[2][NQB][2];  // P, dS as bf16 pairs: [set][block][16-row half]
+  f32x16 sbuf[2], dbuf[2];              // S, dP by block parity
+
+  using Sch = KvSched<NQB, NS, NR>;
+  static_assert(Sch::valid(), "P, dS group placement");
+
+  // P = exp2(S * scale * log2e - lse2) and dS = P * (dP - D) for rows 2e, 2e+1 of
+  // 16-row half sb of block q, packed to bf16 pairs (not pipelined: prologue, epilogue)
+  auto group = [&](auto MASK, const f32x16& sc, const f32x16& dp, int q, int u, f32x2 l2, f32x2 dd, int tile,
+                   u32x4 (&pd_p)[NQB][2], u32x4 (&pd_ds)[NQB][2]) {
+    const int sb = u >> 2, e = u & 3, r0 = 8 * sb + 2 * e;
+    const int qoff = tile * BM + 32 * q + 16 * sb + 8 * h + 2 * e - kcol;  // query - key of row 2e
     float p0 = fast_exp2(__builtin_fmaf(sc[r0], sl, -l2[0]));
     float p1 = fast_exp2(__builtin_fmaf(sc[r0 + 1], sl, -l2[1]));
     if constexpr (decltype(MASK)::value) {  // key kcol is admissible for query q iff kcol <= q
       p0 = (qoff < 0) ? 0.f : p0;
       p1 = (qoff + 1 < 0) ? 0.f : p1;
     }
-    return u32x2{pack_bf16x2(p0, p1), pack_bf16x2(p0 * (dp[r0] - dd[0]), p1 * (dp[r0 + 1] - dd[1]))};
+    pd_p[q][sb][e] = pack_bf16x2(p0, p1);
+    pd_ds[q][sb][e] = pack_bf16x2(p0 * (dp[r0] - dd[0]), p1 * (dp[r0 + 1] - dd[1]));
   };
-  auto stat_pair = [&](const unsigned char* st, int row) {
-    return __builtin_bit_cast(f32x2, *(const __attribute__((address_space(3))) u32x2*)(
-                                          (const __attribute__((address_space(3))) unsigned char*)st + row * 4));
-  };
-
-  // P, dS of the tile being reduced
-  u32x4 pc[NQB][2], dsc[NQB][2];
+  auto stat_row = [&](int q, int u) { return 32 * q + 16 * (u >> 2) + 8 * h + 2 * (u & 3); };
 
   // ---- prologue: fetch tiles i_first and i_first+1, transpose and score i_first
   issue(i_first, 0);
@@ -350,46 +447,38 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   __syncthreads();
   transpose8x8(t_dO ? nat_d(0) : nat_q(0), t_rd, t_dO ? tr_d(0) : tr_q(0), t_wr);
   {
-    auto pro = [&](auto MASK) {
+    constexpr std::integral_constant<bool, CAUSAL> MK{};  // tile i_first always meets the diagonal
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        f32x16 sc = f32x16{}, dp = f32x16{};
+    for (int qb = 0; qb < NQB; ++qb) {
+      f32x16 sc, dp;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const uint32_t off = nb[kk & 1] + qb * NAT_QB + (kk >> 1) * 64 * 16;
-          sc = mfma32(lds_read128(nat_q(0), off), kf[kk], sc);
-          dp = mfma32(lds_read128(nat_d(0), off), vf[kk], dp);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int sb = u >> 2, e = u & 3, row = 32 * qb + 16 * sb + 8 * h + 2 * e;
-          const u32x2 pd = prob_pair(MASK, sc, dp, 8 * sb + 2 * e, stat_pair(st_l(0), row),
-                                     stat_pair(st_d(0), row), i_first * BM + row - kcol);
-          pc[qb][sb][e] = pd[0];
-          dsc[qb][sb][e] = pd[1];
+      for (int kk = 0; kk < NKK; ++kk) {
+        const uint32_t off = nb[kk & 1] + qb * NAT_QB + (kk >> 1) * 64 * 16;
+        const u32x4 aq = lds_read128(nat_q(0), off), ad = lds_read128(nat_d(0), off);
+        if (kk == 0) {
+          sc = mfma32_vz(aq, kf[kk]);
+          dp = mfma32_vz(ad, vf[kk]);
+        } else {
+          mfma32_vacc(sc, aq, kf[kk]);
+          mfma32_vacc(dp, ad, vf[kk]);
         }
       }
-    };
-    if (masked(i_first)) pro(std::true_type{});
-    else pro(std::false_type{});
+      mfma_valu_wait();
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (qb + 1 < NQB || u < 4)  // the last block's groups 4-7 are carried
+          group(MK, sc, dp, qb, u, stat_pair(st_l(0), stat_row(qb, u)), stat_pair(st_d(0), stat_row(qb, u)),
+                i_first, ps[0], dss[0]);
+      sbuf[qb & 1] = sc;
+      dbuf[qb & 1] = dp;
+    }
   }
   __syncthreads();
 
-  // ---- steady state.  Iteration i: reduce tile i (slot cs) while scoring tile i+1
-  // (slot ns), transpose tile i+1 and fetch tile i+2 into slot cs.  One flat, fully
-  // unrolled stream of products per iteration; operand fragments are read kLook
-  // products ahead, and the other work is slotted between products (the order is
-  // pinned with scheduling barriers):
-  //   per 32-query block q:  NS products S, dP (i+1, q), then NR products dV^T, dK^T
-  //   (i, q) with the eight P, dS pair groups of (i+1, q) between them;
-  //   products 0-7 carry the transposition reads, 8-15 its permutes and writes, and
-  //   every fourth product from 16 on one direct copy of tile i+2.
-  constexpr int NS = 2 * NKK, NR = 4 * NDB, NSTEP = NS + NR, T = NQB * NSTEP;
-  constexpr int UNIT_OPS = NR / 8;  // reduce products per P, dS group
-  constexpr int kLook = 4;
-  static_assert(UNIT_OPS >= 1 && 8 * UNIT_OPS == NR, "eight P, dS groups per block");
-  static_assert(16 + 4 * NDMA <= T, "copies must fit in the stream");
-  auto iteration = [&](auto MASK, int i) {
+  // ---- one iteration; PAR = set of the reduced tile, MC / MS = causal mask needed on
+  // the reduced (carried groups) / scored tile
+  auto iteration = [&](auto PARc, auto MC, auto MS, int i) {
+    constexpr int PAR = decltype(PARc)::value;
     const int cs = (i - i_first) & 1, ns = cs ^ 1;
     const int it = i + 1, it2 = min(i + 2, i_last - 1);  // past the end: refetch, unused
     const unsigned char* t_src = t_dO ? nat_d(ns) : nat_q(ns);
@@ -403,22 +492,32 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
       const int m = r - NS, sb = m / (2 * NDB), db = (m >> 1) % NDB;
       return lds_read128((m & 1) ? tr_q(cs) : tr_d(cs), tb[sb] + db * TR_DB + q * 64 * 16);
     };
+    // statistics of the group whose first stage runs after op T0 (read two ops ahead)
+    auto stat_read = [&](auto t_c, f32x2 (&l2)[3], f32x2 (&dd)[3]) {
+      constexpr int ua = Sch::unit_at(decltype(t_c)::value), n = Sch::seq(decltype(t_c)::value) % 3;
+      constexpr bool carry = ua >= 1000;
+      constexpr int q = carry ? NQB - 1 : ua / 16, u = carry ? ua - 1000 : ua % 16;
+      l2[n] = stat_pair(carry ? st_l(cs) : st_l(ns), stat_row(q, u));
+      dd[n] = stat_pair(carry ? st_d(cs) : st_d(ns), stat_row(q, u));
+    };
     u32x4 fr[kLook];
 #pragma unroll
     for (int t = 0; t < kLook; ++t) fr[t] = aread(t);
-    f32x16 sc = f32x16{}, dp = f32x16{};
-    u32x4 pn[NQB][2], dsn[NQB][2];
     u32x4 tx[8];
-    f32x2 sl2[3], sd2[3];  // statistics of the P, dS groups in flight
+    // P, dS groups in flight, by group sequence number mod 3: statistics, stage A -> B
+    // (exponent arguments, dP), stage B -> C (P, dP - D)
+    f32x2 sl2[3], sd2[3], ga[3], gd[3], gp[3], gy[3];
+    static_for<2>([&](auto tc) {
+      if constexpr (Sch::unit_at(decltype(tc)::value) >= 0) stat_read(tc, sl2, sd2);
+    });
     static_for<T>([&](auto tc) {
       constexpr int t = decltype(tc)::value;
       constexpr int q = t / NSTEP, r = t % NSTEP;
       const u32x4 a = fr[t % kLook];
       if constexpr (t + kLook < T) fr[t % kLook] = aread(t + kLook);
-      if constexpr (t < 8) {
-        tx[t] = lds_read128(t_src, t_rd ^ (16u * t));
-      } else if constexpr (t < 16) {
-        constexpr int jj = t - 8;
+      if constexpr (t < 8) tx[t] = lds_read128(t_src, t_rd ^ (16u * t));
+      if constexpr (t >= 8 && (t - 8) % 3 == 0 && (t - 8) / 3 < 8) {
+        constexpr int jj = (t - 8) / 3;
         u32x4 y;
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp)
@@ -426,54 +525,75 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
                            : lo16_pair(tx[2 * pp][jj >> 1], tx[2 * pp + 1][jj >> 1]);
         lds_write128(t_dst, t_wr ^ (16u * jj), y);
       }
-      if constexpr (t >= 16 && (t - 16) % 4 == 0 && (t - 16) / 4 < NDMA) dma_item((t - 16) / 4, it2, cs);
-      // statistics of group u are read two products before the group runs
-      static_for<8>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        if constexpr (r == NS + (u + 1) * UNIT_OPS - 1 - 2) {
-          const int row = 32 * q + 16 * (u >> 2) + 8 * h + 2 * (u & 3);
-          sl2[u % 3] = stat_pair(st_l(ns), row);
-          sd2[u % 3] = stat_pair(st_d(ns), row);
-        }
-      });
+      if constexpr (t >= 2 && (t - 2) % 4 == 0 && (t - 2) / 4 < NDMA) dma_item((t - 2) / 4, it2, cs);
+      if constexpr (t + 2 < T && Sch::unit_at(t + 2) >= 0)
+        stat_read(std::integral_constant<int, t + 2>{}, sl2, sd2);
+      // first read of block q's S, dP by VALU code: the products are inline assembly,
+      // so the wait states after the last of them are explicit
+      if constexpr (Sch::unit_at(t) >= 0 && Sch::unit_at(t) < 1000 && Sch::unit_at(t) % 16 == 0) mfma_valu_wait();
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (r < NS) {
         constexpr int kk = r >> 1;
-        if constexpr (r & 1) dp = mfma32(a, vf[kk], kk == 0 ? f32x16{} : dp);
-        else sc = mfma32(a, kf[kk], kk == 0 ? f32x16{} : sc);
+        // vector-register accumulators: the P, dS groups read them with VALU code
+        if constexpr (r & 1) {
+          if constexpr (kk == 0) dbuf[q & 1] = mfma32_vz(a, vf[kk]);
+          else mfma32_vacc(dbuf[q & 1], a, vf[kk]);
+        } else {
+          if constexpr (kk == 0) sbuf[q & 1] = mfma32_vz(a, kf[kk]);
+          else mfma32_vacc(sbuf[q & 1], a, kf[kk]);
+        }
       } else {
         constexpr int m = r - NS, sb = m / (2 * NDB), db = (m >> 1) % NDB;
-        if constexpr (m & 1) dk[db] = mfma32(a, dsc[q][sb], dk[db]);
-        else dv[db] = mfma32(a, pc[q][sb], dv[db]);
-        if constexpr ((m + 1) % UNIT_OPS == 0) {
-          constexpr int u = m / UNIT_OPS, sb2 = u >> 2, e = u & 3;
-          const int row = 32 * q + 16 * sb2 + 8 * h + 2 * e;
-          const u32x2 pd = prob_pair(MASK, sc, dp, 8 * sb2 + 2 * e, sl2[u % 3], sd2[u % 3], it * BM + row - kcol);
-          pn[q][sb2][e] = pd[0];
-          dsn[q][sb2][e] = pd[1];
+        if constexpr (m & 1) dk[db] = mfma32(a, dss[PAR][q][sb], dk[db]);
+        else dv[db] = mfma32(a, ps[PAR][q][sb], dv[db]);
+      }
+      // P, dS groups: stage C of the group started two ops ago, B of the one started
+      // one op ago, A of the one starting now
+      constexpr int uC = Sch::unit_at(t - 2), uB = Sch::unit_at(t - 1), uA = Sch::unit_at(t);
+      if constexpr (uC >= 0) {
+        constexpr int n = Sch::seq(t - 2) % 3;
+        constexpr bool carry = uC >= 1000;
+        constexpr int gq = carry ? NQB - 1 : uC / 16, gu = carry ? uC - 1000 : uC % 16;
+        const uint32_t pv = pack_bf16x2(gp[n][0], gp[n][1]);
+        const uint32_t dv_ = pack_bf16x2(gp[n][0] * gy[n][0], gp[n][1] * gy[n][1]);
+        constexpr int set = carry ? PAR : (PAR ^ 1);
+        ps[set][gq][gu >> 2][gu & 3] = pv;
+        dss[set][gq][gu >> 2][gu & 3] = dv_;
+      }
+      if constexpr (uB >= 0) {
+        constexpr int n = Sch::seq(t - 1) % 3;
+        constexpr bool carry = uB >= 1000;
+        constexpr int gq = carry ? NQB - 1 : uB / 16, gu = carry ? uB - 1000 : uB % 16;
+        float p0 = fast_exp2(ga[n][0]), p1 = fast_exp2(ga[n][1]);
+        constexpr bool mask = carry ? decltype(MC)::value : decltype(MS)::value;
+        if constexpr (mask) {  // key kcol is admissible for query q iff kcol <= q
+          const int qoff = (carry ? i : it) * BM + stat_row(gq, gu) - kcol;
+          p0 = (qoff < 0) ? 0.f : p0;
+          p1 = (qoff + 1 < 0) ? 0.f : p1;
         }
+        gp[n] = f32x2{p0, p1};
+        gy[n] = f32x2{gd[n][0] - sd2[n][0], gd[n][1] - sd2[n][1]};
+      }
+      if constexpr (uA >= 0) {
+        constexpr int n = Sch::seq(t) % 3;
+        constexpr bool carry = uA >= 1000;
+        constexpr int gq = carry ? NQB - 1 : uA / 16, gu = carry ? uA - 1000 : uA % 16;
+        constexpr int r0 = 8 * (gu >> 2) + 2 * (gu & 3);
+        ga[n] = f32x2{__builtin_fmaf(sbuf[gq & 1][r0], sl, -sl2[n][0]), __builtin_fmaf(sbuf[gq & 1][r0 + 1], sl, -sl2[n][1])};
+        gd[n] = f32x2{dbuf[gq & 1][r0], dbuf[gq & 1][r0 + 1]};
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        pc[qb][sb] = pn[qb][sb];
-        dsc[qb][sb] = dsn[qb][sb];
-      }
     wait_vmem();
     __syncthreads();
   };
-  // The causal mask is needed only on the first tiles (queries before the wave's keys):
-  // masked and unmasked iterations run in two loops of straight-line bodies.  Every
-  // wave passes the same number of barriers, one per iteration.
-  int i = i_first;
-  if constexpr (CAUSAL)
-    for (; i + 1 < i_last && masked(i + 1); ++i) iteration(std::true_type{}, i);
-  for (; i + 1 < i_last; ++i) iteration(std::false_type{}, i);
-  {
+  // last tile: carried groups, then its dV^T, dK^T products (set 0)
+  auto epilogue = [&](auto MC, int i) {
     const int cs = (i - i_first) & 1;
+#pragma unroll
+    for (int u = 4; u < 8; ++u)
+      group(MC, sbuf[(NQB - 1) & 1], dbuf[(NQB - 1) & 1], NQB - 1, u, stat_pair(st_l(cs), stat_row(NQB - 1, u)),
+            stat_pair(st_d(cs), stat_row(NQB - 1, u)), i, ps[0], dss[0]);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -481,10 +601,51 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const uint32_t off = tb[sb] + db * TR_DB + qb * 64 * 16;
-          dv[db] = mfma32(lds_read128(tr_d(cs), off), pc[qb][sb], dv[db]);
-          dk[db] = mfma32(lds_read128(tr_q(cs), off), dsc[qb][sb], dk[db]);
+          dv[db] = mfma32(lds_read128(tr_d(cs), off), ps[0][qb][sb], dv[db]);
+          dk[db] = mfma32(lds_read128(tr_q(cs), off), dss[0][qb][sb], dk[db]);
         }
+  };
+  auto copy_set = [&](int from, int to) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        ps[to][qb][sb] = ps[from][qb][sb];
+        dss[to][qb][sb] = dss[from][qb][sb];
+      }
+  };
+  // Causal: only tiles i_first and i_first+1 can hold queries before some key of the
+  // workgroup (its first key is i_first * BM and it spans 128 keys), so the mask is
+  // needed in the first two iterations at most; they run masked for every wave (the
+  // mask is exact where it is not needed).
+  constexpr std::integral_constant<bool, CAUSAL> C{};
+  constexpr std::false_type F{};
+  constexpr std::integral_constant<int, 0> P0{};
+  constexpr std::integral_constant<int, 1> P1{};
+  int i = i_first;
+  bool last_masked = CAUSAL;  // mask state of the tile left for the epilogue
+  if (i + 1 < i_last) {
+    iteration(P0, C, C, i);  // reduces set 0, scores into set 1
+    ++i;
+    if (i + 1 < i_last) {
+      iteration(P1, C, F, i);  // reduces set 1, scores into set 0
+      ++i;
+      last_masked = false;
+      for (; i + 2 < i_last; i += 2) {
+        iteration(P0, F, F, i);
+        iteration(P1, F, F, i + 1);
+      }
+      if (i + 1 < i_last) {
+        iteration(P0, F, F, i);
+        ++i;
+        copy_set(1, 0);
+      }
+    } else {
+      copy_set(1, 0);
+    }
   }
+  if (CAUSAL && last_masked) epilogue(C, i);
+  else epilogue(F, i);
   if (col_store) {
     // keys padded away for every query get exact zeros
     store_ct_rows<D>(p.dk + head, kcol, dk, col_live ? p.scale : 0.f, h);
