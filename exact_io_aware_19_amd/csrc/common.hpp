@@ -343,12 +343,33 @@ __device__ __forceinline__ constexpr uint32_t swz_unit(uint32_t row, uint32_t ch
   return (row >> 4) * (16 * NCH) + ch * 16 + ((row & 15) ^ ((ch & 3) | (((row >> 4) & 1) * 12)));
 }
 
-// Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix into a swizzled tile,
-// one wave instruction (1 KB) at a time: instruction ii of wave w fills the 64
+// Second swizzle, for tiles that are also read transposed with ds_read_b64_tr_b16: the
+// in-block slot XORed by 4 * (ch % 4).  Measured conflict-free on gfx950 for the MFMA
+// operand reads (16 rows of one block at one chunk) and for transposed reads of 4
+// rows x 16 columns per 16-lane group; the swizzle above conflicts on the latter.
+template <int NCH>
+__device__ __forceinline__ constexpr uint32_t swz4_unit(uint32_t row, uint32_t ch) {
+  return (row >> 4) * (16 * NCH) + ch * 16 + ((row & 15) ^ (4 * (ch & 3)));
+}
+
+// 8 bytes per lane with the gfx950 16-bit transpose read: within each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+// 4j + i / 4, j = 0..3 (checked with a probe).  A lane group that addresses rows
+// k0 + s / 4, columns c0 + 4 (s % 4) .. +3 of a row-major bf16 matrix thus receives
+// column c0 + i, rows k0 .. k0+3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* base, uint32_t byte) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) unsigned char*)base + byte));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix into a swizzled tile
+// (swz_unit, or swz4_unit if SWZ4), one wave instruction (1 KB) at a time: instruction ii of wave w fills the 64
 // consecutive 16-byte units starting at unit 64*(ii*NWAVES + w); the lane filling unit
 // u fetches the (row, chunk) that the swizzle places there.  Rows past N are clamped to
 // N-1 (finite data; callers give them zero weight).
-template <int ROWS, int D, int NWAVES>
+template <int ROWS, int D, int NWAVES, bool SWZ4 = false>
 struct SwzCopy {
   static constexpr int NCH = D / 8;
   static constexpr int PER_WAVE = ROWS * NCH / (NWAVES * 64);  // instructions per wave
@@ -357,7 +378,8 @@ struct SwzCopy {
                                                int ii) {
     const int u = (ii * NWAVES + w) * 64 + l;
     const int blk = u / (16 * NCH), ch = (u % (16 * NCH)) >> 4, slot = u & 15;
-    const int row = min(blk * 16 + (slot ^ ((ch & 3) | ((blk & 1) * 12))), N - 1 - row0);
+    const int x = SWZ4 ? 4 * (ch & 3) : ((ch & 3) | ((blk & 1) * 12));
+    const int row = min(blk * 16 + (slot ^ x), N - 1 - row0);
     buf2lds16(r, (uint32_t)(row * (D * 2) + ch * 16), (uint32_t)row0 * (D * 2),
               tile + (size_t)(ii * NWAVES + w) * 64 * 16);
   }

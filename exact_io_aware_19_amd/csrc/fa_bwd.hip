@@ -43,11 +43,12 @@ template <int D, int BN, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int TILE_BYTES = BN * D * 2;
+  constexpr int NCH = D / 8;
   constexpr int NKB = BN / 32, NDB = D / 32, NKK = D / 16;
-  // LDS: K natural x2, V natural x2, K^T x2
+  // LDS: K x2, V x2 (swz4 layout); K^T operands are read from the K tile transposed
   auto kbuf = [&](int i) { return smem + i * TILE_BYTES; };
   auto vbuf = [&](int i) { return smem + (2 + i) * TILE_BYTES; };
-  auto ktbuf = [&](int i) { return smem + (4 + i) * TILE_BYTES; };
+  using Copy = SwzCopy<BN, D, kDqWaves, true>;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
@@ -112,25 +113,35 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
     return;
   }
   const float sl = p.scale_log2;
-  TrTile<BN, D, kDqThreads> kt;
-  const uint32_t nfrag = NatFrag<D>::base(c, h);  // K and V tiles, A operands of S^T and dP^T
-  const uint32_t tfrag[2] = {TrFrag<BN>::base(c, h, 0), TrFrag<BN>::base(c, h, 1)};  // K^T tile, A operand of dQ^T
+  // Fragment bases.  S^T, dP^T: lane (c, h) reads K / V row 32*kb + row_perm(c), chunk
+  // 2*kk + h; the swizzle depends on kk only through kk % 2.  dQ^T: the K^T operand
+  // (rows d = 32*db + c, k-slots keys 16*sb + 8*h + 0..7 of block kb) comes from two
+  // transposed reads of the K tile (keys +0..3, +4..7): lane s of 16-lane group g
+  // addresses key 8*(g/2) + s/4 (+4 for the second read, an XOR of 64 in the byte
+  // address), columns 16*(g%2) + 4*(s%4) .. +3.
+  const uint32_t rp = row_perm(c);
+  uint32_t nb[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) nb[x] = 16 * swz4_unit<NCH>(rp, 2 * x + h);
+  const int tg = l >> 4, ts = l & 15;
+  const uint32_t trb = 16 * swz4_unit<NCH>(8 * (tg >> 1) + (ts >> 2), 2 * (tg & 1) + ((ts & 3) >> 1)) + 8 * (ts & 1);
+  constexpr uint32_t BLK16 = 16 * NCH * 16;  // bytes per 16 rows
+  auto issue = [&](int t, int s) {
+#pragma unroll
+    for (int ii = 0; ii < Copy::PER_WAVE; ++ii) {
+      Copy::issue(kg, t * BN, N, kbuf(s), w, l, ii);
+      Copy::issue(vg, t * BN, N, vbuf(s), w, l, ii);
+    }
+  };
 
-  load_nat_tile<BN, D, kDqWaves>(kg, 0, N, kbuf(0), w, l);
-  load_nat_tile<BN, D, kDqWaves>(vg, 0, N, vbuf(0), w, l);
-  kt.fetch(kg, 0, N, tid);
+  issue(0, 0);
   wait_vmem();
-  kt.store(ktbuf(0), tid);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
     const bool has_next = t + 1 < ntiles;
-    if (has_next) {
-      load_nat_tile<BN, D, kDqWaves>(kg, (t + 1) * BN, N, kbuf(cur ^ 1), w, l);
-      load_nat_tile<BN, D, kDqWaves>(vg, (t + 1) * BN, N, vbuf(cur ^ 1), w, l);
-      kt.fetch(kg, (t + 1) * BN, N, tid);
-    }
+    if (has_next) issue(t + 1, cur ^ 1);
     const int kt0 = t * BN;
     if (kt0 < wave_kend) {
       bool need_mask = kt0 + BN > kv_end;
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const uint32_t off = nfrag + kb * NatFrag<D>::BLK + kk * NatFrag<D>::KK;
+          const uint32_t off = nb[kk & 1] + kb * 2 * BLK16 + (kk >> 1) * 64 * 16;
           const u32x4 ak = lds_read128(kbuf(cur), off);
           s = mfma32(ak, qf[kk], s);
           const u32x4 av = lds_read128(vbuf(cur), off);
@@ -170,15 +181,13 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const u32x4 a = lds_read128(ktbuf(cur), tfrag[db & 1] + db * TrFrag<BN>::DB + (4 * kb + 2 * sb) * TrFrag<BN>::CH);
-            dq[db] = mfma32(a, dsk[sb], dq[db]);
+            const uint32_t off = (2 * kb + sb) * BLK16 + db * 4 * 16 * 16;
+            const u32x2 a0 = lds_read_tr16(kbuf(cur), trb + off), a1 = lds_read_tr16(kbuf(cur), (trb ^ 64u) + off);
+            dq[db] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, dsk[sb], dq[db]);
           }
       }
     }
-    if (has_next) {
-      wait_vmem();
-      kt.store(ktbuf(cur ^ 1), tid);
-    }
+    wait_vmem();
     __syncthreads();
   }
   if (row_ok) store_ct_rows<D>(p.dq + head, qrow, dq, p.scale, h);
@@ -663,7 +672,7 @@ template <int D, int BN, int BM, bool CAUSAL, bool KVLEN>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
   {
-    constexpr size_t lds = 6ull * BN * D * 2;
+    constexpr size_t lds = 4ull * BN * D * 2;
     auto kern = fa_bwd_dq_kernel<D, BN, CAUSAL, KVLEN>;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
