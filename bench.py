@@ -8,6 +8,11 @@ mask, on the large-head workload (B=2, H=16, N=8192, d=128, bf16 ~ N(0,1), scale
 
 FLOP convention: forward 4*B*H*N^2*d, halved when causal; backward 2.5x the forward.
 `value` = total FLOPs of the K timed steps / their wall time (inputs resident in HBM).
+The backward runs as its two passes (fa_backward_dq_pass, fa_backward_dkdv_pass: the
+same kernels fa_backward launches) so each kernel is timed with its own HIP events.
+Algorithmic FLOPs per kernel (for the roofline): forward 4*B*H*N^2*d; dK/dV pass
+8*B*H*N^2*d (S, dP, dV, dK); dQ pass 2*B*H*N^2*d (dQ; its recomputation of S and dP is
+not algorithmic work); all halved when causal.
 
 Printed JSON line (rank 0 only):
   metric, value (TFLOP/s), unit, n_gpus, steps, warmup, ms_per_step, higher_is_better,
@@ -16,12 +21,22 @@ Printed JSON line (rank 0 only):
   cpu_baseline (the fp64 oracle on a bounded sample, host cores of this machine).
 
 Options: --sweep prints one extra line per workload of the sweep to stderr.
+Profiling helpers (rocprofv3 runs whose summaries are committed under profiles/):
+  --copy-calibration      also time a plain 256 MiB device copy (10 times), the
+                          known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters
+  --summarize-pmc FETCH_CSV WRITE_CSV OUT.md
+                          turn two rocprofv3 --pmc counter CSVs into the traffic summary
+                          that `roofline.traffic` reads (valid while the kernel sources
+                          keep the hash recorded in it)
 """
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -37,6 +52,39 @@ METRIC = "attention fwd/bwd TFLOP/s (bf16, causal & non) + % of MI355X bf16 MFMA
 def fwd_flops(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
+
+
+# algorithmic FLOPs of one kernel launch, as a multiple of the forward's
+KERNEL_FLOP_SHARE = {"fwd": 1.0, "dq": 0.5, "dkdv": 2.0}
+KERNEL_NAME = {"fwd": "fa_fwd_kernel", "dq": "fa_bwd_dq_kernel", "dkdv": "fa_bwd_dkdv_kernel"}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attention_b2h16n8192d128_hbm_traffic.md")
+COPY_CAL_MIB = 256  # plain device copy that calibrates FETCH_SIZE / WRITE_SIZE
+
+
+def kernel_source_hash():
+    """Hash of the HIP/C++ sources of the library: a traffic figure taken on other
+    sources is stale."""
+    src = os.path.join(ROOT, "exact_io_aware_19_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary, or None
+    when there is none or it was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    with open(TRAFFIC_SUMMARY) as f:
+        text = f.read()
+    m = re.search(r"kernel_source_sha: (\w+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(r"^\| %s \| ([0-9.]+) \|" % re.escape(kernel), text, re.M)
+    return float(m.group(1)) if m else None
 
 
 def _alg_bytes(B, H, N, d, direction):
@@ -66,20 +114,25 @@ def run_gpu(args):
     ws = torch.empty(fa.fa_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    calls = [("fwd", False), ("bwd", False), ("fwd", True), ("bwd", True)]
-    ev = {c: [] for c in calls}
+    # one step = forward and backward, no mask then causal; the backward as its two
+    # passes so that every kernel has its own events
+    kern_calls = [("fwd", False), ("dq", False), ("dkdv", False), ("fwd", True), ("dq", True), ("dkdv", True)]
+    ev = {c: [] for c in kern_calls}
+
+    def launch(kind, causal):
+        if kind == "fwd":
+            fa.fa_forward(q, k, v, o[causal], lse[causal], scale, causal, stream=stream)
+        else:
+            fa.fa_backward_pass(kind, q, k, v, o[causal], do, lse[causal], dq, dk, dv, scale, causal, ws,
+                                stream=stream)
 
     def step(record):
-        for c in calls:
-            direction, causal = c
+        for c in kern_calls:
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            if direction == "fwd":
-                fa.fa_forward(q, k, v, o[causal], lse[causal], scale, causal, stream=stream)
-            else:
-                fa.fa_backward(q, k, v, o[causal], do, lse[causal], dq, dk, dv, scale, causal, ws, stream=stream)
+            launch(*c)
             if record:
                 e1.record(stream)
                 ev[c].append((e0, e1))
@@ -93,34 +146,56 @@ def run_gpu(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    kms = {c: sum(a.elapsed_time(b) for a, b in ev[c]) / len(ev[c]) for c in kern_calls}
     step_flops = 0.0
     detail = {}
-    for c in calls:
-        direction, causal = c
-        f = fwd_flops(B, H, N, d, causal) * (1.0 if direction == "fwd" else 2.5)
-        step_flops += f
-        ms = sum(a.elapsed_time(b) for a, b in ev[c]) / len(ev[c])
-        tf = f / (ms * 1e-3) / 1e12
-        detail[f"{direction}_{'causal' if causal else 'full'}"] = {
-            "ms": round(ms, 4),
-            "tflops": round(tf, 1),
-            "pct_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
-            "alg_gbs": round(_alg_bytes(B, H, N, d, direction) / (ms * 1e-3) / 1e9, 1),
-        }
+    for direction in ("fwd", "bwd"):
+        for causal in (False, True):
+            f = fwd_flops(B, H, N, d, causal) * (1.0 if direction == "fwd" else 2.5)
+            step_flops += f
+            ms = kms[("fwd", causal)] if direction == "fwd" else kms[("dq", causal)] + kms[("dkdv", causal)]
+            tf = f / (ms * 1e-3) / 1e12
+            entry = {
+                "ms": round(ms, 4),
+                "tflops": round(tf, 1),
+                "pct_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+                "alg_gbs": round(_alg_bytes(B, H, N, d, direction) / (ms * 1e-3) / 1e9, 1),
+            }
+            if direction == "bwd":
+                entry["dq_pass_ms"] = round(kms[("dq", causal)], 4)
+                entry["dkdv_pass_ms"] = round(kms[("dkdv", causal)], 4)
+            detail[f"{direction}_{'causal' if causal else 'full'}"] = entry
     value = step_flops * args.steps / wall / 1e12
-    # dominant launch = the call with the largest share of the step time
-    dom = max(detail, key=lambda kname: detail[kname]["ms"])
-    dd = detail[dom]
+    # dominant kernel = the one with the largest share of the step time
+    dom = max(kern_calls, key=lambda c: kms[c])
+    kind, causal = dom
+    dom_flops = KERNEL_FLOP_SHARE[kind] * fwd_flops(B, H, N, d, causal)
+    achieved = dom_flops / (kms[dom] * 1e-3) / 1e12
+    kname = f"{KERNEL_NAME[kind]}<{d}, {64 if d == 128 else 128}, {'true' if causal else 'false'}, false>"
     roofline = {
         "bound": "mfma",
-        "achieved": dd["tflops"],
+        "achieved": round(achieved, 1),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
-        "frac": round(dd["tflops"] / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
-        "launch": dom,
-        "launch_kernels": (["fa_fwd_kernel"] if dom.startswith("fwd") else ["fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"]),
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": read_traffic(kname),
+        "kernel": kname,
+        "kernel_ms": round(kms[dom], 4),
+        "algorithmic_flops_per_launch": dom_flops,
     }
+    if args.copy_calibration:
+        nbytes = COPY_CAL_MIB << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        roofline["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(e0.elapsed_time(e1) / 10, 4)}
     sweep = []
     if args.sweep:
         sweep = run_sweep(fa, wl, torch, dev, stream)
@@ -206,6 +281,64 @@ def cpu_baseline(inp, shape, heads):
     }
 
 
+def summarize_pmc(fetch_csv, write_csv, out_md):
+    """HBM bytes per launch of every kernel of the bench step from two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the last ten plain copies (bench.py --copy-calibration), whose
+    bytes are known."""
+
+    def load(path, counter):
+        rows = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return sorted(rows)
+
+    out = {}
+    cal = {}
+    kib = COPY_CAL_MIB * 1024  # KiB each calibration copy reads and writes
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = load(path, counter)
+        copies = [v for _, name, v in rows if "copyBuffer" in name][-10:]
+        if len(copies) < 10:
+            raise SystemExit(f"{path}: fewer than 10 copy dispatches (run bench.py with --copy-calibration)")
+        cal[counter] = sum(copies) / len(copies)  # KiB per copy
+        per = {}
+        for _, name, v in rows:
+            if "fa355" in name:
+                key = name.replace("void fa355::(anonymous namespace)::", "").split("(")[0]
+                per.setdefault(key, []).append(v)
+        out[counter] = {kname: sum(vs) / len(vs) for kname, vs in per.items()}
+    m = re.search(r"--copy-calibration (\d+)", " ".join(sys.argv))
+    lines = [
+        "# HBM traffic per launch, attention fwd/bwd, B=2 H=16 N=8192 d=128",
+        "",
+        "Commands (each on the GPU box, from the repository root, one counter per run):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration",
+        "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration",
+        "    python bench.py --summarize-pmc gpurun_out/pmc_fetch/p_counter_collection.csv gpurun_out/pmc_write/p_counter_collection.csv " + os.path.relpath(out_md, ROOT),
+        "",
+        "Calibration: the last ten dispatches of the plain %d MiB device copy read and write" % COPY_CAL_MIB,
+        "%d bytes each; the counters read %.0f KiB (FETCH_SIZE) and %.0f KiB (WRITE_SIZE)," % (COPY_CAL_MIB << 20, cal["FETCH_SIZE"], cal["WRITE_SIZE"]),
+        "so bytes = counter KiB x %.4f x 1024 (fetch) and x %.4f x 1024 (write)." % (kib / cal["FETCH_SIZE"], kib / cal["WRITE_SIZE"]),
+        "",
+        "kernel_source_sha: " + kernel_source_hash(),
+        "",
+        "| kernel | HBM bytes per launch | fetch bytes | write bytes |",
+        "|---|---|---|---|",
+    ]
+    for kname in sorted(out["FETCH_SIZE"]):
+        fb = out["FETCH_SIZE"][kname] * 1024 * kib / cal["FETCH_SIZE"]
+        wb = out["WRITE_SIZE"].get(kname, 0.0) * 1024 * kib / cal["WRITE_SIZE"]
+        lines.append("| %s | %.0f | %.0f | %.0f |" % (kname, fb + wb, fb, wb))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,7 +347,13 @@ def main(argv=None):
     ap.add_argument("--n", type=int, default=8192, help="sequence length of the bench workload (default 8192)")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="also time every workload of the sweep (stderr)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"also run 10 plain device copies of {COPY_CAL_MIB} MiB (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2

@@ -10,6 +10,7 @@ Low-level calls with the C names (caller allocates every output):
     fa_backward(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
                 kv_len=None, stream=None)
     fa_backward_workspace_size(B, H, N, d)
+    fa_backward_pass(which, ...)  # "dq" or "dkdv": the two passes of fa_backward
 
 Convenience wrappers that allocate outputs with torch:
     forward(q, k, v, causal=False, scale=None, kv_len=None) -> (o, lse)
@@ -27,6 +28,7 @@ __all__ = [
     "fa_forward",
     "fa_backward",
     "fa_backward_workspace_size",
+    "fa_backward_pass",
     "forward",
     "backward",
     "FAError",
@@ -110,6 +112,20 @@ def fa_backward(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_
 
     workspace: a GPU tensor (any dtype) of at least fa_backward_workspace_size bytes.
     """
+    _backward_call(None, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len, stream)
+
+
+def fa_backward_pass(which, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len=None, stream=None):
+    """C ``fa_backward_dq_pass`` (which="dq") or ``fa_backward_dkdv_pass`` (which="dkdv").
+
+    The two passes in that order on one stream are exactly ``fa_backward``.
+    """
+    if which not in ("dq", "dkdv"):
+        raise ValueError("which must be 'dq' or 'dkdv'")
+    _backward_call(which, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len, stream)
+
+
+def _backward_call(which, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len, stream):
     _check_qkv("q", q)
     shape = tuple(q.shape)
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
@@ -124,7 +140,11 @@ def fa_backward(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_
     sp = _stream_ptr(stream, q.device)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
             dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal))]
-    if kvp is None:
+    if which is not None:
+        name = f"fa_backward_{which}_pass"
+        st = getattr(lib, name)(*args, kvp, workspace.data_ptr(), nbytes, sp)
+        _lib.check(st, name)
+    elif kvp is None:
         st = lib.fa_backward(*args, workspace.data_ptr(), nbytes, sp)
         _lib.check(st, "fa_backward")
     else:

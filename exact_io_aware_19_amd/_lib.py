@@ -28,6 +28,8 @@ EXPORTED = (
     "fa_backward_workspace_size",
     "fa_backward",
     "fa_backward_kvlen",
+    "fa_backward_dq_pass",
+    "fa_backward_dkdv_pass",
     "fa_status_string",
 )
 
@@ -55,6 +57,10 @@ def load():
     lib.fa_backward.restype = i
     lib.fa_backward_kvlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.fa_backward_kvlen.restype = i
+    for name in ("fa_backward_dq_pass", "fa_backward_dkdv_pass"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+        fn.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib

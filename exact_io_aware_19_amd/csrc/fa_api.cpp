@@ -64,7 +64,7 @@ size_t workspace_bytes(int B, int H, int N, int d) {
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                  const int32_t* kv_len, void* workspace, size_t ws_bytes, fa_stream_t stream) {
+                  const int32_t* kv_len, void* workspace, size_t ws_bytes, fa_stream_t stream, int passes = 3) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -95,7 +95,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.causal = causal != 0;
-  return fa355::launch_backward(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return fa355::launch_backward(a, (hipStream_t)stream, passes) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -129,6 +129,22 @@ int fa_backward_kvlen(const void* q, const void* k, const void* v, const void* o
                       const int32_t* kv_len, void* workspace, size_t workspace_bytes_, fa_stream_t stream) {
   return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, kv_len, workspace,
                        workspace_bytes_, stream);
+}
+
+int fa_backward_dq_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                        int causal, const int32_t* kv_len, void* workspace, size_t workspace_bytes_,
+                        fa_stream_t stream) {
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, kv_len, workspace,
+                       workspace_bytes_, stream, 1);
+}
+
+int fa_backward_dkdv_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                          int causal, const int32_t* kv_len, void* workspace, size_t workspace_bytes_,
+                          fa_stream_t stream) {
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, kv_len, workspace,
+                       workspace_bytes_, stream, 2);
 }
 
 const char* fa_status_string(int status) {

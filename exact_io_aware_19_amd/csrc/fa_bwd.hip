@@ -54,8 +54,10 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
   const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
   const int BH = p.B * p.H;
   const int nqb = (p.N + kDqBM - 1) / kDqBM;
-  const int qbi = CAUSAL ? (nqb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
+  // no mask: each XCD works through whole heads; causal: heaviest query blocks first
+  int blk, bh;
+  block_order<!CAUSAL>((int)blockIdx.x, nqb, BH, blk, bh);
+  const int qbi = CAUSAL ? (nqb - 1 - blk) : blk;
   const int b = bh / p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
@@ -304,8 +306,11 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   // wave index as a scalar: tile copies then compute their LDS destinations in SALU
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 31, h = l >> 5;
   const int BH = p.B * p.H;
-  const int kbi = blockIdx.x / BH;  // causal: key block 0 sees the most queries, so it goes first
-  const int bh = blockIdx.x % BH;
+  // no mask: each XCD works through whole heads; causal: key block 0 sees the most
+  // queries, so it goes first
+  const int nkb = (p.N + kKvBN - 1) / kKvBN;
+  int kbi, bh;
+  block_order<!CAUSAL>((int)blockIdx.x, nkb, BH, kbi, bh);
   const int b = bh / p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
@@ -669,9 +674,9 @@ hipError_t set_lds(K kern, size_t lds) {
 }
 
 template <int D, int BN, int BM, bool CAUSAL, bool KVLEN>
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int passes) {
   const unsigned bh = (unsigned)(a.B * a.H);
-  {
+  if (passes & 1) {
     constexpr size_t lds = 4ull * BN * D * 2;
     auto kern = fa_bwd_dq_kernel<D, BN, CAUSAL, KVLEN>;
     hipError_t e = set_lds(kern, lds);
@@ -681,7 +686,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (passes & 2) {
     constexpr size_t lds = KvLds<D, BM>::BYTES;
     auto kern = fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN>;
     hipError_t e = set_lds(kern, lds);
@@ -690,20 +695,21 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), lds, stream, a);
     return hipGetLastError();
   }
+  return hipSuccess;
 }
 
 template <int D, int BN, int BM>
-hipError_t dispatch_masks(const BwdArgs& a, hipStream_t s) {
+hipError_t dispatch_masks(const BwdArgs& a, hipStream_t s, int ps) {
   const bool kv = a.kv_len != nullptr;
-  if (a.causal) return kv ? launch_bwd<D, BN, BM, true, true>(a, s) : launch_bwd<D, BN, BM, true, false>(a, s);
-  return kv ? launch_bwd<D, BN, BM, false, true>(a, s) : launch_bwd<D, BN, BM, false, false>(a, s);
+  if (a.causal) return kv ? launch_bwd<D, BN, BM, true, true>(a, s, ps) : launch_bwd<D, BN, BM, true, false>(a, s, ps);
+  return kv ? launch_bwd<D, BN, BM, false, true>(a, s, ps) : launch_bwd<D, BN, BM, false, false>(a, s, ps);
 }
 
 }  // namespace
 
-hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return dispatch_masks<128, 64, 64>(a, stream);
-  return dispatch_masks<64, 128, 128>(a, stream);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream, int passes) {
+  if (a.d == 128) return dispatch_masks<128, 64, 64>(a, stream, passes);
+  return dispatch_masks<64, 128, 128>(a, stream, passes);
 }
 
 }  // namespace fa355

@@ -50,10 +50,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
   const int BH = p.B * p.H;
   const int nqb = (p.N + kBM - 1) / kBM;
-  // Causal: heaviest query blocks first.  Consecutive workgroups take consecutive
-  // heads, so every workgroup of one head lands on the same XCD when B*H % 8 == 0.
-  const int qbi = CAUSAL ? (nqb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
+  // no mask: each XCD works through whole heads; causal: heaviest query blocks first
+  int blk, bh;
+  block_order<!CAUSAL>((int)blockIdx.x, nqb, BH, blk, bh);
+  const int qbi = CAUSAL ? (nqb - 1 - blk) : blk;
   const int b = bh / p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;

@@ -40,6 +40,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+// passes: bit 0 = dQ pass (dq + row statistics), bit 1 = dK/dV pass
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream, int passes = 3);
 
 }  // namespace fa355

@@ -102,6 +102,27 @@ int fa_backward_kvlen(const void* q, const void* k, const void* v, const void* o
                       void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
                       const int32_t* kv_len, void* workspace, size_t workspace_bytes, fa_stream_t stream);
 
+/*
+ * The two passes of the backward, for callers that schedule them separately and for
+ * per-kernel timing: fa_backward_kvlen(args) is exactly fa_backward_dq_pass(args)
+ * followed by fa_backward_dkdv_pass(args) on the same stream.  Arguments, validation
+ * and error codes are those of fa_backward_kvlen (kv_len: device int32[B] or NULL for
+ * no padding).
+ *   fa_backward_dq_pass:   writes dq and the row statistics D_i and LSE_i * log2(e)
+ *                          into the workspace (dk, dv are not touched);
+ *   fa_backward_dkdv_pass: reads those statistics and writes dk and dv (dq is not
+ *                          touched); it must follow a dQ pass on the same inputs and
+ *                          workspace, in stream order.
+ */
+int fa_backward_dq_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                        int causal, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                        fa_stream_t stream);
+int fa_backward_dkdv_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                          int causal, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                          fa_stream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);
 

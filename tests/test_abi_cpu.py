@@ -103,3 +103,19 @@ def test_backward_rejects_bad_args(lib):
     assert _bwd(lib, dq=FAKE + 4) == -7
     assert lib.fa_backward_kvlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 0.1, 0, FAKE,
                                  None, 0, None) == -5
+
+
+@pytest.mark.parametrize("name", ["fa_backward_dq_pass", "fa_backward_dkdv_pass"])
+def test_backward_passes_validate_like_backward(lib, name):
+    fn = getattr(lib, name)
+    need = lib.fa_backward_workspace_size(1, 1, 16, 64)
+
+    def call(q=FAKE, d=64, N=16, ws=FAKE, ws_bytes=need, kv=None):
+        return fn(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, N, d, 0.125, 0, kv, ws, ws_bytes, None)
+
+    assert call(q=None) == -1
+    assert call(d=32) == -3
+    assert call(N=0) == -2
+    assert call(ws=None) == -5
+    assert call(ws_bytes=need - 1) == -5
+    assert call(ws=FAKE + 16) == -7

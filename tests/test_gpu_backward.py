@@ -144,3 +144,29 @@ def test_backward_rejects_small_workspace(gpu):
         fa.fa_backward(q, q, q, o, q, lse, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), 0.125,
                        False, ws)
     assert e.value.status == -5
+
+
+@pytest.mark.parametrize("causal,kvlen", [(False, False), (True, False), (False, True)])
+def test_backward_passes_compose_to_backward(gpu, causal, kvlen):
+    """fa_backward_dq_pass then fa_backward_dkdv_pass == fa_backward, bit for bit; each
+    pass writes only its own outputs."""
+    import torch
+    import exact_io_aware_19_amd as fa
+
+    B, H, N, d = 2, 2, 333, 128
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(gpu) for _ in range(4))
+    kv = torch.tensor([200, 333], dtype=torch.int32, device=gpu) if kvlen else None
+    o, lse = fa.forward(q, k, v, causal=causal, kv_len=kv)
+    ref = fa.backward(q, k, v, o, do, lse, causal=causal, kv_len=kv)
+    ws = torch.empty(fa.fa_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=gpu)
+    sentinel = torch.full_like(q, 7.0)
+    dq, dk, dv = sentinel.clone(), sentinel.clone(), sentinel.clone()
+    fa.fa_backward_pass("dq", q, k, v, o, do, lse, dq, dk, dv, d ** -0.5, causal, ws, kv_len=kv)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, sentinel) and torch.equal(dv, sentinel)
+    assert torch.equal(dq.view(torch.int16), ref[0].view(torch.int16))
+    fa.fa_backward_pass("dkdv", q, k, v, o, do, lse, dq, dk, dv, d ** -0.5, causal, ws, kv_len=kv)
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), ref):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
