@@ -173,6 +173,12 @@ __device__ __forceinline__ void g2lds16(const void* gptr, unsigned char* lds_wav
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier that completes this wave's LDS operations but leaves its global
+// loads (register loads and direct-to-LDS copies) in flight; __syncthreads() also waits
+// for those.  Data copied into LDS must be waited for (wait_vmem) before a barrier that
+// publishes it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------------------------
 // Buffer-resource loads.  One resource per head matrix ([N][D] bf16, at most 16 MiB):
 // the tile offset travels in the scalar soffset operand and each lane's offset inside
@@ -265,60 +271,6 @@ __device__ __forceinline__ void load_nat_tile(buf_rsrc r, int row0, int N, unsig
     }
   }
 }
-
-// Register-staged transposed tile: fetch() issues the global loads, store() writes the
-// transposed 4x4 blocks to LDS (after the loads have landed).
-template <int ROWS, int D, int NTHREADS>
-struct TrTile {
-  static constexpr int NBLK = (ROWS / 4) * (D / 4) / NTHREADS;
-  static_assert(NBLK >= 1 && NBLK * NTHREADS == (ROWS / 4) * (D / 4), "tile must split evenly over the threads");
-  u32x2 r[NBLK][4];
-
-  __device__ __forceinline__ void fetch(buf_rsrc rs, int row0, int N, int tid) {
-    const uint32_t soff = (uint32_t)row0 * (D * 2);
-    if (row0 + ROWS <= N) {  // uniform branch: the common case needs no clamping at all
-#pragma unroll
-      for (int i = 0; i < NBLK; ++i) {
-        const int vb = tid + i * NTHREADS;
-        const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
-        const int k0 = kc * 8 + hsel * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[i][j] = buf_load64(rs, (uint32_t)((k0 + j) * (D * 2) + dq * 8), soff);
-      }
-    } else {
-      const int lim = N - 1 - row0;
-#pragma unroll
-      for (int i = 0; i < NBLK; ++i) {
-        const int vb = tid + i * NTHREADS;
-        const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
-        const int k0 = kc * 8 + hsel * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[i][j] = buf_load64(rs, (uint32_t)(min(k0 + j, lim) * (D * 2) + dq * 8), soff);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(unsigned char* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
-      const int vb = tid + i * NTHREADS;
-      const int hsel = vb & 1, dq = (vb >> 1) % (D / 4), kc = (vb >> 1) / (D / 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // column j of the 4x4 block: (X[k0..k0+3][4*dq + j])
-        const int half = j >> 1;
-        u32x2 out;
-        if (j & 1) {
-          out[0] = hi16_pair(r[i][0][half], r[i][1][half]);
-          out[1] = hi16_pair(r[i][2][half], r[i][3][half]);
-        } else {
-          out[0] = lo16_pair(r[i][0][half], r[i][1][half]);
-          out[1] = lo16_pair(r[i][2][half], r[i][3][half]);
-        }
-        lds_write64(tile, bcm_tr_byte<ROWS / 8>(dq * 4 + j, kc) + hsel * 8, out);
-      }
-    }
-  }
-};
 
 // Per-lane base byte offsets of MFMA A-operand fragments.
 //  natural tile [R][D]: lane (h, c) reads row 32*blk + row_perm(c), chunk 2*kk + h

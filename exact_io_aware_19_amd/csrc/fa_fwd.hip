@@ -34,6 +34,41 @@ constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr float kRescaleTau = 8.0f;
 constexpr int kLdsTiles = 4;  // 2 K tiles + 2 V^T tiles
 
+// Register-staged transposition of one half of a V tile (rows [BN/2 * part, +BN/2)) by
+// the 256 threads of one wave group: each thread moves one 4x4 bf16 block (4 keys x 4
+// head-dim columns) into the transposed [D][BN] tile, one 8-byte column at a time.
+template <int BN, int D>
+struct VtHalf {
+  static_assert((BN / 2 / 4) * (D / 4) == 256, "one 4x4 block per thread of a wave group");
+  u32x2 r[4];
+  int k0, dq, kc, hsel;
+  __device__ __forceinline__ void init(int t, int part) {
+    hsel = t & 1;
+    dq = (t >> 1) % (D / 4);
+    kc = part * (BN / 16) + (t >> 1) / (D / 4);
+    k0 = kc * 8 + hsel * 4;
+  }
+  __device__ __forceinline__ void fetch(buf_rsrc rs, int row0, int N) {
+    const int lim = N - 1 - row0;  // rows past N repeat row N-1 (finite; their P is 0)
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (D * 2));  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = buf_load64(rs, (uint32_t)(min(k0 + j, lim) * (D * 2) + dq * 8), soff);
+  }
+  // column j of the block: (V[k0 .. k0+3][4*dq + j])
+  __device__ __forceinline__ void store(unsigned char* tile, int j) const {
+    const int half = j >> 1;
+    u32x2 out;
+    if (j & 1) {
+      out[0] = hi16_pair(r[0][half], r[1][half]);
+      out[1] = hi16_pair(r[2][half], r[3][half]);
+    } else {
+      out[0] = lo16_pair(r[0][half], r[1][half]);
+      out[1] = lo16_pair(r[2][half], r[3][half]);
+    }
+    lds_write64(tile, bcm_tr_byte<BN / 8>(dq * 4 + j, kc) + hsel * 8, out);
+  }
+};
+
 template <int D, int BN, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -102,7 +137,20 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   float l_run = 0.f;        // this lane's partial row sum (the other half-wave holds the rest)
   const float sl = p.scale_log2;
 
-  TrTile<BN, D, kThreads> vt;
+  const int grp = w >> 2, wg = w & 3;  // wave group (one wave per SIMD) and wave in it
+  VtHalf<BN, D> vh;
+  vh.init(tid & 255, grp);
+  // one wave-instruction of the K tile copy by wave group 0 (4 per wave)
+  constexpr int KCOPY = BN * (D / 8) / (4 * 64);
+  auto k_copy = [&](int row0, unsigned char* tile, int ii) {
+    const int pos = (ii * 4 + wg) * 64 + l;  // unit index written by this lane
+    const int blk = pos / (16 * (D / 8)), rem = pos % (16 * (D / 8));
+    const int row = min(blk * 16 + (rem & 15), N - 1 - row0);
+    // the LDS destination (M0) and the tile offset (soffset) are wave-uniform
+    const int slot = __builtin_amdgcn_readfirstlane(ii * 4 + wg);
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (D * 2));
+    buf2lds16(kg, (uint32_t)(row * (D * 2) + (rem >> 4) * 16), soff, tile + (size_t)slot * 64 * 16);
+  };
   const uint32_t kfrag = NatFrag<D>::base(c, h);  // K tile, A operand of S^T
   const uint32_t vfrag[2] = {TrFrag<BN>::base(c, h, 0), TrFrag<BN>::base(c, h, 1)};  // V^T tile, A operand of O^T
 
@@ -117,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   constexpr int NS = NKB * NKK;       // Q K^T MFMAs of one tile
   constexpr int kLook = 4;
   f32x16 s[NKB];  // scores of the next tile to go through the softmax
-  auto mfma_stream = [&](auto first_c, auto count_c, const unsigned char* vb_, const unsigned char* kt) {
+  auto mfma_stream = [&](auto first_c, auto count_c, const unsigned char* vb_, const unsigned char* kt, auto&& side) {
     constexpr int F = decltype(first_c)::value, M = decltype(count_c)::value;
     // flat MFMA index i: [0, NPV) = P V^T (kb, sb, db), [NPV, NPV+NS) = Q K^T (kk, kb)
     auto read_frag = [&](int i) -> u32x4 {
@@ -131,33 +179,63 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
     u32x4 fr[kLook];
 #pragma unroll
     for (int i = 0; i < kLook && i < M; ++i) fr[i] = read_frag(F + i);
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
+    static_for<M>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       const u32x4 a = fr[i % kLook];
-      if (i + kLook < M) fr[i % kLook] = read_frag(F + i + kLook);
+      if constexpr (i + kLook < M) fr[i % kLook] = read_frag(F + i + kLook);
       __builtin_amdgcn_sched_barrier(0);
-      const int fi = F + i;
-      if (fi < NPV) {
-        const int kb = fi / (2 * NDB), sb = (fi / NDB) % 2, db = fi % NDB;
+      constexpr int fi = F + i;
+      if constexpr (fi < NPV) {
+        constexpr int kb = fi / (2 * NDB), sb = (fi / NDB) % 2, db = fi % NDB;
         o[db] = mfma32(a, pk[kb][sb], o[db]);
       } else {
         // kb fastest: the NKB accumulation chains alternate, so no MFMA waits on the
         // result of the one issued just before it
-        const int kk = (fi - NPV) / NKB, kb = (fi - NPV) % NKB;
+        constexpr int kk = (fi - NPV) / NKB, kb = (fi - NPV) % NKB;
         s[kb] = mfma32(a, qf[kk], kk == 0 ? f32x16{} : s[kb]);
       }
+      side(std::integral_constant<int, i>{}, std::integral_constant<int, M>{});
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
+  // Tile movement rides on the MFMA operation: operation j of a wave group writes its
+  // half of V_{j+1}^T (fetched into registers during its preceding softmax), and wave
+  // group 0 also starts the copy of K_{j+2}.  Both spread over the MFMA stream, a few
+  // products apart, so no wave stalls on a burst of memory instructions.
+  //
+  // The V^T stores are unconditional, so the stream has no branches: operation -1 stores
+  // V_0 (fetched before the loop), and the store of the last operation rewrites a
+  // buffer no later phase reads.  The K copy is chosen per stream at compile time.
   auto op_mfma = [&](int j) {  // j = -1: scores of tile 0 only
     const bool do_pv = j >= 0 && j < ntiles && j * BN < wave_kend;
     const int jn = j + 1;
     const bool do_s = jn < ntiles && jn * BN < wave_kend;
+    unsigned char* vnext = vbuf(jn & 1);
+    unsigned char* knext = kbuf(j & 1);
+    const int krow = (j + 2) * BN;
     const unsigned char* vb_ = vbuf(j & 1);
     const unsigned char* kt = kbuf(jn & 1);
-    if (do_pv && do_s) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV + NS>{}, vb_, kt);
-    else if (do_pv) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV>{}, vb_, kt);
-    else if (do_s) mfma_stream(std::integral_constant<int, NPV>{}, std::integral_constant<int, NS>{}, vb_, kt);
+    auto run = [&](auto cpk) {
+      constexpr bool CPK = decltype(cpk)::value;
+      auto side = [&](auto ic, auto mc) {
+        constexpr int i = decltype(ic)::value, SP = decltype(mc)::value / 16;
+        if constexpr (i % (2 * SP) == SP % 2 && i / (2 * SP) < 4) vh.store(vnext, i / (2 * SP));  // V^T columns
+        if constexpr (CPK && i % (4 * SP) == 2 && i / (4 * SP) < KCOPY) k_copy(krow, knext, i / (4 * SP));
+      };
+      if (do_pv && do_s) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV + NS>{}, vb_, kt, side);
+      else if (do_pv) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV>{}, vb_, kt, side);
+      else if (do_s) mfma_stream(std::integral_constant<int, NPV>{}, std::integral_constant<int, NS>{}, vb_, kt, side);
+      else {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) vh.store(vnext, c4);
+        if constexpr (CPK) {
+#pragma unroll
+          for (int ii = 0; ii < KCOPY; ++ii) k_copy(krow, knext, ii);
+        }
+      }
+    };
+    if (grp == 0 && j + 2 < ntiles) run(std::true_type{});
+    else run(std::false_type{});
   };
 
   // VALU operation for tile j: mask, online softmax with conditional rescaling, P -> pk.
@@ -212,41 +290,35 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   // Every wave runs  [S_0] softmax_0 [PV_0,S_1] softmax_1 [PV_1,S_2] ...  Waves 0-3
   // (group 0) and 4-7 (group 1) hold one wave per SIMD each and run this sequence one
   // phase apart, so in every phase one wave of each SIMD issues MFMAs while the other
-  // runs the softmax on the VALU.  Each phase ends with a workgroup barrier.  Tile
-  // loads: even phase 2j issues K_{j+1} and V_j (register staged); odd phase 2j+1 stores
-  // V_j^T before its barrier.  MFMA operation j (PV_j, S_{j+1}) runs in phases 2j+2 and
-  // 2j+3, so both rings are two deep: a buffer is refilled only after both groups used it.
-  const int grp = w >> 2;
-  auto begin_phase = [&](int ph) {
-    if (ph & 1) return;
-    const int j = ph >> 1;
-    if (j + 1 < ntiles) load_nat_tile<BN, D, kWaves>(kg, (j + 1) * BN, N, kbuf((j + 1) & 1), w, l);
-    if (j < ntiles) vt.fetch(vg, j * BN, N, tid);
-  };
-  auto end_phase = [&](int ph) {
-    if (ph & 1) {
-      const int j = ph >> 1;
-      if (j < ntiles) {
-        wait_vmem();
-        vt.store(vbuf(j & 1), tid);
-      }
-    }
-    __syncthreads();
-  };
-
+  // runs the softmax on the VALU.  Each phase ends with a workgroup barrier.
+  // MFMA operation j (PV_j, S_{j+1}) runs in phase 2j+2 (group 0) and 2j+3 (group 1).
+  // Tile movement:
+  //   V_{j+1}: each group fetches its half into registers at the start of its softmax_j
+  //            and writes it transposed during its MFMA operation j (phases 2j+2, 2j+3);
+  //   K_{j+2}: group 0 starts the copy during its MFMA operation j (phase 2j+2) and
+  //            waits for it at the end of its softmax_{j+1} (phase 2j+3).
+  // Both land before the barrier that ends phase 2j+3, in buffers whose previous
+  // contents (V_{j-1}, K_j) were last read in phase 2j+1, so both rings are two deep.
+  // V_0 is fetched here and written by MFMA operation -1 (phases 0 and 1).
   load_nat_tile<BN, D, kWaves>(kg, 0, N, kbuf(0), w, l);
+  vh.fetch(vg, 0, N);
   wait_vmem();
   __syncthreads();
   // operation index of group 0 in phase ph is ph, of group 1 is ph - 1:
   //   op 0 = S_0, op 2j+1 = softmax_j, op 2j+2 = (PV_j, S_{j+1})
   for (int ph = 0; ph < 2 * ntiles + 2; ++ph) {
-    begin_phase(ph);
     const int op = ph - grp;
     if (op >= 0) {
-      if (op & 1) op_softmax(op >> 1);
-      else op_mfma((op >> 1) - 1);
+      if (op & 1) {
+        const int j = op >> 1;
+        if (j + 1 < ntiles) vh.fetch(vg, (j + 1) * BN, N);
+        op_softmax(j);
+        if (grp == 0) wait_vmem();
+      } else {
+        op_mfma((op >> 1) - 1);
+      }
     }
-    end_phase(ph);
+    lds_barrier();
   }
 
   // ---- epilogue: normalise once, store O and LSE
