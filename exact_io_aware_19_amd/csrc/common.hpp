@@ -91,17 +91,30 @@ __device__ __forceinline__ float half_sum(float x) {
 
 // Max / sum of the 16*NB values of NB C fragments as balanced trees (depth log2, not
 // a serial chain).
+// The max tree takes three inputs per node (v_max3_f32): about half the instructions of
+// a binary tree.
 template <int NB>
 __device__ __forceinline__ float tree_max(const f32x16 (&v)[NB]) {
-  float t[8 * NB];
+  constexpr int NV = 16 * NB;
+  float t[NV];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t[8 * b + i] = fmaxf(v[b][2 * i], v[b][2 * i + 1]);
+    for (int i = 0; i < 16; ++i) t[16 * b + i] = v[b][i];
+  int n = NV;
 #pragma unroll
-  for (int n = 4 * NB; n >= 1; n >>= 1)
+  for (int lvl = 0; lvl < 8; ++lvl) {
+    if (n == 1) break;
+    const int m = (n + 2) / 3;  // nodes of this level; the last one may take 1 or 2 inputs
 #pragma unroll
-    for (int i = 0; i < n; ++i) t[i] = fmaxf(t[i], t[i + n]);
+    for (int i = 0; i < m; ++i) {
+      const int a = 3 * i;
+      if (a + 2 < n) t[i] = __builtin_fmaxf(__builtin_fmaxf(t[a], t[a + 1]), t[a + 2]);
+      else if (a + 1 < n) t[i] = __builtin_fmaxf(t[a], t[a + 1]);
+      else t[i] = t[a];
+    }
+    n = m;
+  }
   return t[0];
 }
 template <int NB>
