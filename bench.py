@@ -87,13 +87,15 @@ def read_traffic(kernel):
     return float(m.group(1)) if m else None
 
 
-def _alg_bytes(B, H, N, d, direction):
+def _alg_bytes(B, H, N, d, direction, hkv=None):
     """Algorithmic HBM bytes of one call: fwd reads Q,K,V and writes O (bf16) + LSE (fp32);
-    bwd reads Q,K,V,O,dO (bf16) + LSE, writes dQ,dK,dV (bf16), writes and reads D (fp32)."""
+    bwd reads Q,K,V,O,dO (bf16) + LSE, writes dQ,dK,dV (bf16), writes and reads D (fp32).
+    With grouped K/V heads (hkv < H) the K, V, dK, dV terms count hkv heads."""
     rows = B * H * N
+    kv_rows = B * (hkv or H) * N
     if direction == "fwd":
-        return 8.0 * rows * d + 4.0 * rows
-    return 16.0 * rows * d + 12.0 * rows
+        return 4.0 * rows * d + 4.0 * kv_rows * d + 4.0 * rows
+    return 8.0 * rows * d + 8.0 * kv_rows * d + 12.0 * rows
 
 
 def run_gpu(args):
@@ -205,7 +207,8 @@ def run_gpu(args):
 def run_sweep(fa, wl, torch, dev, stream, iters=10):
     out = []
     for name in ["tiny", "bert_large", "gpt2"] + [f"sweep_n{n}_{m}" for n in (2048, 4096, 8192, 16384)
-                                                   for m in ("full", "causal")] + ["long_64k"]:
+                                                   for m in ("full", "causal")] + ["long_64k", "gqa_n8192",
+                                                                                   "mqa_n4096"]:
         w = wl.get_workload(name)
         inp = wl.generate(w)
         t = inp.to_torch(dev)
@@ -213,17 +216,24 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
         o = torch.empty_like(t["q"])
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         res = {"workload": name}
+        grouped = w.kv_heads != w.H
+        if grouped:
+            res["h_kv"] = w.kv_heads
         for direction in (("fwd", "bwd") if w.backward else ("fwd",)):
             if direction == "fwd":
-                def call():
-                    fa.fa_forward(t["q"], t["k"], t["v"], o, lse, w.scale, w.causal, kv_len=t["kv_len"], stream=stream)
-            else:
-                dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
-                ws = torch.empty(fa.fa_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+                fwd = fa.fa_forward_gqa if grouped else fa.fa_forward
 
                 def call():
-                    fa.fa_backward(t["q"], t["k"], t["v"], o, t["do"], lse, dq, dk, dv, w.scale, w.causal, ws,
-                                   kv_len=t["kv_len"], stream=stream)
+                    fwd(t["q"], t["k"], t["v"], o, lse, w.scale, w.causal, kv_len=t["kv_len"], stream=stream)
+            else:
+                dq = torch.empty_like(t["q"])
+                dk, dv = torch.empty_like(t["k"]), torch.empty_like(t["v"])
+                ws = torch.empty(fa.fa_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+                bwd = fa.fa_backward_gqa if grouped else fa.fa_backward
+
+                def call():
+                    bwd(t["q"], t["k"], t["v"], o, t["do"], lse, dq, dk, dv, w.scale, w.causal, ws,
+                        kv_len=t["kv_len"], stream=stream)
             for _ in range(3):
                 call()
             torch.cuda.synchronize()
@@ -238,7 +248,7 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
             tf = f / (ms * 1e-3) / 1e12
             res[direction] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                               "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
-                              "alg_gbs": round(_alg_bytes(B, H, N, d, direction) / (ms * 1e-3) / 1e9, 1)}
+                              "alg_gbs": round(_alg_bytes(B, H, N, d, direction, w.kv_heads) / (ms * 1e-3) / 1e9, 1)}
         print(json.dumps({"sweep": res}), file=sys.stderr, flush=True)
         out.append(res)
         del t, o, lse

@@ -11,8 +11,13 @@ Low-level calls with the C names (caller allocates every output):
                 kv_len=None, stream=None)
     fa_backward_workspace_size(B, H, N, d)
     fa_backward_pass(which, ...)  # "dq" or "dkdv": the two passes of fa_backward
+    fa_forward_gqa(q, k, v, o, lse, scale, causal, kv_len=None, stream=None)
+    fa_backward_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
+                    kv_len=None, stream=None)
+        grouped K/V heads: k, v, dk, dv are [B, H_kv, N, d] with H_kv dividing H
 
-Convenience wrappers that allocate outputs with torch:
+Convenience wrappers that allocate outputs with torch (grouped K/V heads when k has
+fewer heads than q):
     forward(q, k, v, causal=False, scale=None, kv_len=None) -> (o, lse)
     backward(q, k, v, o, dout, lse, causal=False, scale=None, kv_len=None) -> (dq, dk, dv)
 
@@ -29,6 +34,8 @@ __all__ = [
     "fa_backward",
     "fa_backward_workspace_size",
     "fa_backward_pass",
+    "fa_forward_gqa",
+    "fa_backward_gqa",
     "forward",
     "backward",
     "FAError",
@@ -102,6 +109,61 @@ def fa_forward(q, k, v, o, lse, scale, causal, kv_len=None, stream=None):
         _lib.check(st, "fa_forward_kvlen")
 
 
+def _kv_shape(q, k):
+    """[B, H_kv, N, d] of grouped K/V heads for q of shape [B, H, N, d]."""
+    B, H, N, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, H_kv, {N}, {d}]")
+    hkv = int(k.shape[1])
+    if hkv < 1 or H % hkv:
+        raise ValueError(f"K/V heads ({hkv}) must divide query heads ({H})")
+    return (B, hkv, N, d)
+
+
+def fa_forward_gqa(q, k, v, o, lse, scale, causal, kv_len=None, stream=None):
+    """C ``fa_forward_gqa``: k, v are [B, H_kv, N, d]; fills o and lse in place."""
+    _check_qkv("q", q)
+    shape = tuple(q.shape)
+    kv_shape = _kv_shape(q, k)
+    _check_qkv("k", k, kv_shape)
+    _check_qkv("v", v, kv_shape)
+    _check_qkv("o", o, shape)
+    _check_lse(lse, shape)
+    B, H, N, d = shape
+    lib = _lib.load()
+    kvp = _kv_ptr(kv_len, B, q.device)
+    sp = _stream_ptr(stream, q.device)
+    st = lib.fa_forward_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+                            kv_shape[1], N, d, float(scale), int(bool(causal)), kvp, sp)
+    _lib.check(st, "fa_forward_gqa")
+
+
+def fa_backward_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len=None, stream=None):
+    """C ``fa_backward_gqa``: k, v, dk, dv are [B, H_kv, N, d]; fills dq, dk, dv in place.
+
+    workspace: a GPU tensor of at least fa_backward_workspace_size(B, H, N, d) bytes.
+    """
+    _check_qkv("q", q)
+    shape = tuple(q.shape)
+    kv_shape = _kv_shape(q, k)
+    for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _check_qkv(name, t, kv_shape)
+    for name, t in (("o", o), ("dout", dout), ("dq", dq)):
+        _check_qkv(name, t, shape)
+    _check_lse(lse, shape)
+    B, H, N, d = shape
+    lib = _lib.load()
+    nbytes = workspace.numel() * workspace.element_size()
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    kvp = _kv_ptr(kv_len, B, q.device)
+    sp = _stream_ptr(stream, q.device)
+    st = lib.fa_backward_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, kv_shape[1], N, d, float(scale),
+                             int(bool(causal)), kvp, workspace.data_ptr(), nbytes, sp)
+    _lib.check(st, "fa_backward_gqa")
+
+
 def fa_backward_workspace_size(B, H, N, d):
     """C ``fa_backward_workspace_size``."""
     return int(_lib.load().fa_backward_workspace_size(B, H, N, d))
@@ -162,7 +224,10 @@ def forward(q, k, v, causal=False, scale=None, kv_len=None):
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_forward(q, k, v, o, lse, _default_scale(d, scale), causal, kv_len=kv_len)
+    if k.dim() == 4 and k.shape[1] != H:
+        fa_forward_gqa(q, k, v, o, lse, _default_scale(d, scale), causal, kv_len=kv_len)
+    else:
+        fa_forward(q, k, v, o, lse, _default_scale(d, scale), causal, kv_len=kv_len)
     return o, lse
 
 
@@ -171,9 +236,13 @@ def backward(q, k, v, o, dout, lse, causal=False, scale=None, kv_len=None, works
     torch = _torch()
     B, H, N, d = q.shape
     dq = torch.empty_like(q)
-    dk = torch.empty_like(q)
-    dv = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
     if workspace is None:
         workspace = torch.empty(fa_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
-    fa_backward(q, k, v, o, dout, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace, kv_len=kv_len)
+    if k.dim() == 4 and k.shape[1] != H:
+        fa_backward_gqa(q, k, v, o, dout, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace,
+                        kv_len=kv_len)
+    else:
+        fa_backward(q, k, v, o, dout, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace, kv_len=kv_len)
     return dq, dk, dv

@@ -20,6 +20,7 @@ STATUS_NAMES = {
     -5: "FA_ERR_WORKSPACE",
     -6: "FA_ERR_LAUNCH",
     -7: "FA_ERR_ALIGN",
+    -8: "FA_ERR_KVHEADS",
 }
 
 EXPORTED = (
@@ -30,6 +31,8 @@ EXPORTED = (
     "fa_backward_kvlen",
     "fa_backward_dq_pass",
     "fa_backward_dkdv_pass",
+    "fa_forward_gqa",
+    "fa_backward_gqa",
     "fa_status_string",
 )
 
@@ -61,6 +64,10 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
         fn.restype = i
+    lib.fa_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
+    lib.fa_forward_gqa.restype = i
+    lib.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz, vp]
+    lib.fa_backward_gqa.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib

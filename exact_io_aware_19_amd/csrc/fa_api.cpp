@@ -27,12 +27,16 @@ int check_shape(int B, int H, int N, int d) {
 
 int check_scale(float scale) { return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE; }
 
+int check_kv_heads(int H, int Hkv) { return (Hkv >= 1 && H % Hkv == 0) ? FA_OK : FA_ERR_KVHEADS; }
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                 float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                 int d, float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  st = check_kv_heads(H, Hkv);
   if (st != FA_OK) return st;
   st = check_scale(scale);
   if (st != FA_OK) return st;
@@ -46,6 +50,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   a.kv_len = kv_len;
   a.B = B;
   a.H = H;
+  a.Hkv = Hkv;
   a.N = N;
   a.d = d;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -63,10 +68,12 @@ size_t workspace_bytes(int B, int H, int N, int d) {
 }
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                  void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
                   const int32_t* kv_len, void* workspace, size_t ws_bytes, fa_stream_t stream, int passes = 3) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  st = check_kv_heads(H, Hkv);
   if (st != FA_OK) return st;
   st = check_scale(scale);
   if (st != FA_OK) return st;
@@ -90,6 +97,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   a.ws_l = (float*)workspace + (size_t)B * H * a.nw;
   a.B = B;
   a.H = H;
+  a.Hkv = Hkv;
   a.N = N;
   a.d = d;
   a.scale = scale;
@@ -104,12 +112,17 @@ extern "C" {
 
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, fa_stream_t stream) {
-  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, stream);
+  return forward_impl(q, k, v, o, lse, B, H, H, N, d, scale, causal, nullptr, stream);
 }
 
 int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                      float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
-  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, kv_len, stream);
+  return forward_impl(q, k, v, o, lse, B, H, H, N, d, scale, causal, kv_len, stream);
+}
+
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+                   int d, float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
+  return forward_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, kv_len, stream);
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
@@ -120,14 +133,21 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d) {
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
                 size_t workspace_bytes_, fa_stream_t stream) {
-  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, nullptr, workspace,
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, nullptr, workspace,
                        workspace_bytes_, stream);
 }
 
 int fa_backward_kvlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
                       const int32_t* kv_len, void* workspace, size_t workspace_bytes_, fa_stream_t stream) {
-  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, kv_len, workspace,
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, kv_len, workspace,
+                       workspace_bytes_, stream);
+}
+
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
+                    const int32_t* kv_len, void* workspace, size_t workspace_bytes_, fa_stream_t stream) {
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, kv_len, workspace,
                        workspace_bytes_, stream);
 }
 
@@ -135,7 +155,7 @@ int fa_backward_dq_pass(const void* q, const void* k, const void* v, const void*
                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                         int causal, const int32_t* kv_len, void* workspace, size_t workspace_bytes_,
                         fa_stream_t stream) {
-  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, kv_len, workspace,
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, kv_len, workspace,
                        workspace_bytes_, stream, 1);
 }
 
@@ -143,7 +163,7 @@ int fa_backward_dkdv_pass(const void* q, const void* k, const void* v, const voi
                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                           int causal, const int32_t* kv_len, void* workspace, size_t workspace_bytes_,
                           fa_stream_t stream) {
-  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, kv_len, workspace,
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, kv_len, workspace,
                        workspace_bytes_, stream, 2);
 }
 
@@ -157,6 +177,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned (lse 4, workspace 256)";
+    case FA_ERR_KVHEADS: return "FA_ERR_KVHEADS: H_kv must be >= 1 and divide H";
     default: return "unknown fa_status";
   }
 }

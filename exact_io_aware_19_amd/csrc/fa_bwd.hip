@@ -61,8 +61,10 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
   const int b = bh / p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
-  const buf_rsrc kg = make_rsrc(p.k + head, (uint32_t)N * D * 2);
-  const buf_rsrc vg = make_rsrc(p.v + head, (uint32_t)N * D * 2);
+  // grouped K/V heads: the H / Hkv query heads of a group share one K/V head
+  const size_t kv_head = (size_t)(b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * N * D;
+  const buf_rsrc kg = make_rsrc(p.k + kv_head, (uint32_t)N * D * 2);
+  const buf_rsrc vg = make_rsrc(p.v + kv_head, (uint32_t)N * D * 2);
 
   int kv_end = N;
   if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);
@@ -287,7 +289,7 @@ struct KvSched {
   }
 };
 
-template <int D, int BM, bool CAUSAL, bool KVLEN>
+template <int D, int BM, bool CAUSAL, bool KVLEN, bool GROUPED>
 __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   using L = KvLds<D, BM>;
@@ -305,19 +307,30 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   const int tid = threadIdx.x;
   // wave index as a scalar: tile copies then compute their LDS destinations in SALU
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 31, h = l >> 5;
-  const int BH = p.B * p.H;
+  // one workgroup per (key block, K/V head); with grouped heads it runs the query tiles
+  // of every query head of its group in turn and sums their dK, dV in registers
+  const int BHkv = p.B * p.Hkv;
   // no mask: each XCD works through whole heads; causal: key block 0 sees the most
   // queries, so it goes first
   const int nkb = (p.N + kKvBN - 1) / kKvBN;
-  int kbi, bh;
-  block_order<!CAUSAL>((int)blockIdx.x, nkb, BH, kbi, bh);
-  const int b = bh / p.H;
+  int kbi, bhk;
+  block_order<!CAUSAL>((int)blockIdx.x, nkb, BHkv, kbi, bhk);
+  const int b = bhk / p.Hkv;
   const int N = p.N;
-  const size_t head = (size_t)bh * N * D;
-  const buf_rsrc qg = make_rsrc(p.q + head, (uint32_t)N * D * 2);
-  const buf_rsrc dog = make_rsrc(p.dout + head, (uint32_t)N * D * 2);
-  const float* __restrict__ wl = p.ws_l + (size_t)bh * p.nw;
-  const float* __restrict__ wd = p.ws_d + (size_t)bh * p.nw;
+  const int G = GROUPED ? p.H / p.Hkv : 1;          // query heads per K/V head
+  const int bq0 = b * p.H + (bhk - b * p.Hkv) * G;  // first query head of the group
+  const size_t head = (size_t)bhk * N * D;          // K, V, dK, dV
+  buf_rsrc qg, dog;
+  const float* __restrict__ wl;
+  const float* __restrict__ wd;
+  auto set_query_head = [&](int g) {
+    const size_t qhead = (size_t)(bq0 + g) * N * D;
+    qg = make_rsrc(p.q + qhead, (uint32_t)N * D * 2);
+    dog = make_rsrc(p.dout + qhead, (uint32_t)N * D * 2);
+    wl = p.ws_l + (size_t)(bq0 + g) * p.nw;
+    wd = p.ws_d + (size_t)(bq0 + g) * p.nw;
+  };
+  set_query_head(0);
 
   int kv_end = N;
   if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);
@@ -455,6 +468,7 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   auto stat_row = [&](int q, int u) { return 32 * q + 16 * (u >> 2) + 8 * h + 2 * (u & 3); };
 
   // ---- prologue: fetch tiles i_first and i_first+1, transpose and score i_first
+  auto prologue = [&]() {
   issue(i_first, 0);
   issue(min(i_first + 1, i_last - 1), 1);
   wait_vmem();
@@ -488,6 +502,7 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     }
   }
   __syncthreads();
+  };
 
   // ---- one iteration; PAR = set of the reduced tile, MC / MS = causal mask needed on
   // the reduced (carried groups) / scored tile
@@ -636,30 +651,57 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   constexpr std::false_type F{};
   constexpr std::integral_constant<int, 0> P0{};
   constexpr std::integral_constant<int, 1> P1{};
-  int i = i_first;
-  bool last_masked = CAUSAL;  // mask state of the tile left for the epilogue
-  if (i + 1 < i_last) {
-    iteration(P0, C, C, i);  // reduces set 0, scores into set 1
-    ++i;
-    if (i + 1 < i_last) {
-      iteration(P1, C, F, i);  // reduces set 1, scores into set 0
-      ++i;
-      last_masked = false;
+  if constexpr (GROUPED) {
+    // The query heads of the group run one after another, each through the whole
+    // pipeline; dK, dV keep accumulating.  Causal: every iteration runs masked (exact
+    // where no mask is needed), which keeps to two iteration variants.
+    constexpr std::integral_constant<bool, CAUSAL> M{};
+    for (int g = 0; g < G; ++g) {
+      if (g > 0) {
+        // the previous head's epilogue has read its last tiles before the copies refill them
+        __syncthreads();
+        set_query_head(g);
+      }
+      prologue();
+      int i = i_first;
       for (; i + 2 < i_last; i += 2) {
-        iteration(P0, F, F, i);
-        iteration(P1, F, F, i + 1);
+        iteration(P0, M, M, i);
+        iteration(P1, M, M, i + 1);
       }
       if (i + 1 < i_last) {
-        iteration(P0, F, F, i);
+        iteration(P0, M, M, i);
         ++i;
         copy_set(1, 0);
       }
-    } else {
-      copy_set(1, 0);
+      epilogue(M, i);
     }
+  } else {
+    prologue();
+    int i = i_first;
+    bool last_masked = CAUSAL;  // mask state of the tile left for the epilogue
+    if (i + 1 < i_last) {
+      iteration(P0, C, C, i);  // reduces set 0, scores into set 1
+      ++i;
+      if (i + 1 < i_last) {
+        iteration(P1, C, F, i);  // reduces set 1, scores into set 0
+        ++i;
+        last_masked = false;
+        for (; i + 2 < i_last; i += 2) {
+          iteration(P0, F, F, i);
+          iteration(P1, F, F, i + 1);
+        }
+        if (i + 1 < i_last) {
+          iteration(P0, F, F, i);
+          ++i;
+          copy_set(1, 0);
+        }
+      } else {
+        copy_set(1, 0);
+      }
+    }
+    if (CAUSAL && last_masked) epilogue(C, i);
+    else epilogue(F, i);
   }
-  if (CAUSAL && last_masked) epilogue(C, i);
-  else epilogue(F, i);
   if (col_store) {
     // keys padded away for every query get exact zeros
     store_ct_rows<D>(p.dk + head, kcol, dk, col_live ? p.scale : 0.f, h);
@@ -688,10 +730,11 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int passes) {
   }
   if (passes & 2) {
     constexpr size_t lds = KvLds<D, BM>::BYTES;
-    auto kern = fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN>;
+    auto kern = a.Hkv != a.H ? fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN, true>
+                             : fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN, false>;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)((a.N + kKvBN - 1) / kKvBN) * bh;
+    const unsigned grid = (unsigned)((a.N + kKvBN - 1) / kKvBN) * (unsigned)(a.B * a.Hkv);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), lds, stream, a);
     return hipGetLastError();
   }

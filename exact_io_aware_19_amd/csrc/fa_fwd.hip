@@ -92,9 +92,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   const int b = bh / p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
+  // grouped K/V heads: the H / Hkv query heads of a group share one K/V head
+  const size_t kv_head = (size_t)(b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * N * D;
   const uint16_t* __restrict__ qg = p.q + head;
-  const buf_rsrc kg = make_rsrc(p.k + head, (uint32_t)N * D * 2);
-  const buf_rsrc vg = make_rsrc(p.v + head, (uint32_t)N * D * 2);
+  const buf_rsrc kg = make_rsrc(p.k + kv_head, (uint32_t)N * D * 2);
+  const buf_rsrc vg = make_rsrc(p.v + kv_head, (uint32_t)N * D * 2);
 
   int kv_end = N;
   if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);

@@ -13,6 +13,7 @@ struct FwdArgs {
   float* lse;
   const int32_t* kv_len;  // device int32[B] or nullptr
   int B, H, N, d;
+  int Hkv;           // K/V heads; query head h reads K/V head h / (H / Hkv)
   float scale_log2;  // scale * log2(e)
   int causal;
 };
@@ -34,6 +35,7 @@ struct BwdArgs {
   float* ws_l;  // LSE_i * log2(e), +inf where the row has no admissible key, fp32 [B][H][nw]
   int nw;
   int B, H, N, d;
+  int Hkv;           // K/V heads; query head h reads K/V head h / (H / Hkv)
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   int causal;

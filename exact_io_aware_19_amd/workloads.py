@@ -10,9 +10,10 @@ evaluation and results paragraphs: BERT-large, GPT-2, long-context up to 64K tok
 used: every tensor is i.i.d. N(0, 1) drawn in fp32 from numpy's PCG64 and rounded to
 bf16 (round to nearest, ties to even).
 
-Draw order per workload (one generator per workload seed): q, k, v (each
-[B, H, N, d] float32), then dO, then the key-padding lengths, then the indices of
-the key rows scaled x8, then the sampled query rows.
+Draw order per workload (one generator per workload seed): q ([B, H, N, d] float32),
+k, v ([B, H_kv, N, d]; H_kv = H unless the workload groups its K/V heads), then dO,
+then the key-padding lengths, then the indices of the key rows scaled x8, then the
+sampled query rows.
 """
 
 from dataclasses import dataclass, field
@@ -45,10 +46,15 @@ class Workload:
     sampled_rows: int = 0          # oracle checks only these query rows (0 = all)
     backward: bool = True
     note: str = ""
+    h_kv: int = 0                  # K/V heads (grouped-query attention); 0 = H
 
     @property
     def shape(self):
         return (self.B, self.H, self.N, self.d)
+
+    @property
+    def kv_heads(self):
+        return self.h_kv or self.H
 
     def fwd_flops(self):
         """4 B H N^2 d, halved when causal (the convention of the throughput metric)."""
@@ -75,6 +81,10 @@ WORKLOADS = {
     "long_64k": Workload("long_64k", 1, 16, 65536, 64, True, 1.0 / 8, 1005, scaled_key_frac=0.01,
                          sampled_rows=64, backward=False,
                          note="long-context causal forward; 1% of key rows x8; 64 sampled query rows"),
+    "gqa_n8192": Workload("gqa_n8192", 2, 16, 8192, 128, True, 1.0 / math.sqrt(128), 1006, h_kv=4,
+                          note="grouped K/V heads (4 query heads per K/V head), causal, large-head shape"),
+    "mqa_n4096": Workload("mqa_n4096", 2, 16, 4096, 128, False, 1.0 / math.sqrt(128), 1007, h_kv=1,
+                          note="multi-query attention (one K/V head), large-head shape"),
 }
 
 
@@ -104,7 +114,7 @@ def bf16_bits_to_f64(bits):
 class Inputs:
     workload: Workload
     q: np.ndarray          # uint16 bf16 bits [B,H,N,d]
-    k: np.ndarray
+    k: np.ndarray          # [B,H_kv,N,d]
     v: np.ndarray
     do: np.ndarray = None
     kv_len: np.ndarray = None        # int32 [B] or None
@@ -138,10 +148,14 @@ def generate(w, with_do=None, shape_override=None):
     if isinstance(w, str):
         w = WORKLOADS[w]
     B, H, N, d = shape_override or w.shape
+    group = w.H // w.kv_heads  # query heads per K/V head, kept by a shape override
+    if H % group:
+        raise ValueError(f"{H} query heads do not split into groups of {group}")
+    hkv = H // group
     rng = np.random.default_rng(w.seed)
     qf = rng.standard_normal((B, H, N, d), dtype=np.float32)
-    kf = rng.standard_normal((B, H, N, d), dtype=np.float32)
-    vf = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    kf = rng.standard_normal((B, hkv, N, d), dtype=np.float32)
+    vf = rng.standard_normal((B, hkv, N, d), dtype=np.float32)
     if with_do is None:
         with_do = w.backward
     dof = rng.standard_normal((B, H, N, d), dtype=np.float32) if with_do else None

@@ -57,7 +57,8 @@ typedef enum {
   FA_ERR_SCALE = -4,     /* scale is not finite or not > 0                        */
   FA_ERR_WORKSPACE = -5, /* backward workspace NULL or smaller than required     */
   FA_ERR_LAUNCH = -6,    /* a kernel launch failed (hipGetLastError)             */
-  FA_ERR_ALIGN = -7      /* a tensor pointer is not 16-byte aligned              */
+  FA_ERR_ALIGN = -7,     /* a tensor pointer is not 16-byte aligned              */
+  FA_ERR_KVHEADS = -8    /* H_kv < 1 or H_kv does not divide H (grouped heads)   */
 } fa_status;
 
 /*
@@ -122,6 +123,27 @@ int fa_backward_dkdv_pass(const void* q, const void* k, const void* v, const voi
                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                           int causal, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
                           fa_stream_t stream);
+
+/*
+ * Grouped-query and multi-query attention (GQA, MQA): H query heads share H_kv K/V
+ * heads, query head h using K/V head h / (H / H_kv) (groups of consecutive query
+ * heads); H_kv = H is ordinary multi-head attention and H_kv = 1 is MQA.  The
+ * "FlashAttention" concept wiki page lists GQA/MQA among its open questions (section
+ * 未解決の問い) without defining it; the result here is that of ordinary attention
+ * with every K/V head repeated for the query heads of its group, so dk and dv are the
+ * sums over the group of the per-query-head gradients.
+ *   q, o, dout, dq: [B][H][N][d];  k, v, dk, dv: [B][H_kv][N][d];  lse: [B][H][N].
+ * kv_len: device int32[B] or NULL for no padding.  Everything else (masks, scale,
+ * alignment, workspace of fa_backward_workspace_size(B, H, N, d) bytes, ownership and
+ * errors) is as in fa_forward_kvlen / fa_backward_kvlen; H_kv < 1 or H % H_kv != 0
+ * returns FA_ERR_KVHEADS.  The backward is deterministic: each K/V head's dk and dv
+ * accumulate its group's query heads in a fixed order, in registers.
+ */
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+                   int d, float scale, int causal, const int32_t* kv_len, fa_stream_t stream);
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
+                    const int32_t* kv_len, void* workspace, size_t workspace_bytes, fa_stream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);

@@ -158,6 +158,41 @@ def attention_backward(q, k, v, do, scale, causal=False, kv_len=None):
     return dq, dk, dv
 
 
+def _kv_group(H, Hkv):
+    """Query heads per K/V head; query head h reads K/V head h // G."""
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"K/V heads ({Hkv}) must divide query heads ({H})")
+    return H // Hkv
+
+
+def attention_forward_gqa(q, k, v, scale, causal=False, kv_len=None):
+    """Grouped-query / multi-query attention forward.  q: [B,H,N,d]; k, v: [B,Hkv,N,d]
+    with Hkv dividing H.
+
+    The "FlashAttention" concept wiki page names GQA/MQA among its open questions
+    (section 未解決の問い) without defining it.  Reading: consecutive query heads form
+    the groups, query head h uses K/V head h // (H / Hkv), and the result is ordinary
+    attention with each K/V head repeated for its group -- written out as that repeat.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    G = _kv_group(q.shape[1], k.shape[1])
+    return attention_forward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), scale, causal=causal,
+                             kv_len=kv_len)
+
+
+def attention_backward_gqa(q, k, v, do, scale, causal=False, kv_len=None):
+    """Gradients of L = sum(O * dO) for grouped K/V heads: dQ [B,H,N,d]; dK, dV
+    [B,Hkv,N,d].  A repeated K/V head receives the sum of the gradients of its copies
+    (chain rule through the repeat in attention_forward_gqa)."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    G = _kv_group(H, Hkv)
+    dq, dk, dv = attention_backward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), do, scale, causal=causal,
+                                    kv_len=kv_len)
+    return dq, dk.reshape(B, Hkv, G, N, d).sum(axis=2), dv.reshape(B, Hkv, G, N, d).sum(axis=2)
+
+
 def forward_rows(q, k, v, scale, rows, causal=False, kv_len_b=None):
     """O and LSE of a few query rows of ONE head (q,k,v: [N,d]); for sampled checks at
     sizes where the full forward would be slow.  Each row is computed independently

@@ -13,7 +13,10 @@ Kinds of pin used (no page prints a numeric example, so none is a page value):
   * central finite differences of L = sum(O * dO) for the backward;
   * closed forms and invariants: rows of the softmax sum to one, constant V, the first
     causal row, uniform attention at scale 0, two keys, key shift, key padding,
-    permutation equivariance, zero column sum of dK;
+    permutation equivariance, zero column sum of dK, identical query heads of a K/V
+    group (grouped heads);
+  * library special case for grouped K/V heads: torch scaled_dot_product_attention
+    with enable_gqa=True, forward and autograd;
   * the blocked online recurrence equals the two-pass definition for any block size.
 """
 
@@ -336,6 +339,63 @@ def pin_online_equals_two_pass(ref, online):
                         np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-12)
 
 
+def pin_torch_sdpa_gqa(ref, online):
+    """Grouped K/V heads against torch's own grouped-query attention (enable_gqa) in
+    float64, forward and autograd backward, under every mask mode; MQA included."""
+    import torch
+    import torch.nn.functional as F
+
+    for seed, (H, Hkv, N, d) in enumerate([(4, 2, 11, 4), (6, 3, 16, 8), (4, 1, 9, 4)]):
+        for mode in MASK_MODES:
+            rng, q, _, _, do = _inputs(1600 + seed, 2, H, N, d, with_do=True)
+            k = rng.standard_normal((2, Hkv, N, d))
+            v = rng.standard_normal((2, Hkv, N, d))
+            causal, kv = _mask_args(mode, rng, 2, N)
+            scale = 0.45
+            o, lse = ref.attention_forward_gqa(q, k, v, scale, causal=causal, kv_len=kv)
+            dq, dk, dv = ref.attention_backward_gqa(q, k, v, do, scale, causal=causal, kv_len=kv)
+            for b in range(2):
+                kl = None if kv is None else kv[b]
+                m = _torch_mask(N, causal, kl)
+                tq, tk, tv = (torch.from_numpy(x[b].copy()).requires_grad_(True) for x in (q, k, v))
+                to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale, enable_gqa=True)
+                to.backward(torch.from_numpy(do[b]))
+                np.testing.assert_allclose(o[b], to.detach().numpy(), rtol=0, atol=1e-12)
+                np.testing.assert_allclose(dq[b], tq.grad.numpy(), rtol=0, atol=1e-11)
+                np.testing.assert_allclose(dk[b], tk.grad.numpy(), rtol=0, atol=1e-11)
+                np.testing.assert_allclose(dv[b], tv.grad.numpy(), rtol=0, atol=1e-11)
+                # LSE: per query head against its own K/V head (h // G), torch logsumexp
+                G = H // Hkv
+                for h in range(H):
+                    s = torch.from_numpy(q[b, h]) @ torch.from_numpy(k[b, h // G]).T * scale
+                    s = s.masked_fill(~m, float("-inf"))
+                    np.testing.assert_allclose(lse[b, h], torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def pin_gqa_identical_heads(ref, online):
+    """Closed form: when all G query heads of a group carry the same Q and dO, every
+    query head sees the same attention, so dK and dV are G times the single-head
+    gradients and each O head equals the single-head output."""
+    rng = _rng(1700)
+    for G in (2, 3):
+        N, d = 10, 4
+        q1 = rng.standard_normal((1, 1, N, d))
+        do1 = rng.standard_normal((1, 1, N, d))
+        k = rng.standard_normal((1, 1, N, d))
+        v = rng.standard_normal((1, 1, N, d))
+        for causal in (False, True):
+            o1, _ = ref.attention_forward(q1, k, v, 0.6, causal=causal)
+            _, dk1, dv1 = ref.attention_backward(q1, k, v, do1, 0.6, causal=causal)
+            q = np.repeat(q1, G, axis=1)
+            do = np.repeat(do1, G, axis=1)
+            o, _ = ref.attention_forward_gqa(q, k, v, 0.6, causal=causal)
+            _, dk, dv = ref.attention_backward_gqa(q, k, v, do, 0.6, causal=causal)
+            for h in range(G):
+                np.testing.assert_allclose(o[0, h], o1[0, 0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(dk, G * dk1, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dv, G * dv1, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_golden_two_key,
     pin_bruteforce_forward,
@@ -353,6 +413,8 @@ ALL_PINS = [
     pin_dk_columns_sum_to_zero,
     pin_sampled_rows_match_full,
     pin_online_equals_two_pass,
+    pin_torch_sdpa_gqa,
+    pin_gqa_identical_heads,
 ]
 
 

@@ -30,9 +30,10 @@ def to_np_bf16(t):
     return wl.bf16_bits_to_f64(bits)
 
 
-def custom_inputs(B, H, N, d, seed, causal=False, kv_range=None, with_do=True, scale=None, scaled_key_frac=0.0):
+def custom_inputs(B, H, N, d, seed, causal=False, kv_range=None, with_do=True, scale=None, scaled_key_frac=0.0,
+                  h_kv=0):
     w = wl.Workload(f"custom_{B}x{H}x{N}x{d}", B, H, N, d, causal, scale or 1.0 / np.sqrt(d), seed,
-                    kv_len_range=kv_range, scaled_key_frac=scaled_key_frac, backward=with_do)
+                    kv_len_range=kv_range, scaled_key_frac=scaled_key_frac, backward=with_do, h_kv=h_kv)
     return wl.generate(w)
 
 

@@ -119,3 +119,28 @@ def test_backward_passes_validate_like_backward(lib, name):
     assert call(ws=None) == -5
     assert call(ws_bytes=need - 1) == -5
     assert call(ws=FAKE + 16) == -7
+
+
+@pytest.mark.parametrize("H,Hkv,status", [(4, 3, -8), (4, 0, -8), (4, -2, -8), (4, 5, -8), (0, 1, -2)])
+def test_gqa_entry_points_reject_bad_kv_heads(lib, H, Hkv, status):
+    assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, H, Hkv, 16, 64, 0.125, 0, None, None) == status
+    need = lib.fa_backward_workspace_size(1, max(H, 1), 16, 64)
+    assert lib.fa_backward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, H, Hkv, 16, 64, 0.125, 0,
+                               None, FAKE, need, None) == status
+
+
+def test_gqa_entry_points_validate_like_the_others(lib):
+    assert lib.fa_forward_gqa(None, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, 0.125, 0, None, None) == -1
+    assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 96, 0.125, 0, None, None) == -3
+    assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, 0.0, 0, None, None) == -4
+    assert lib.fa_forward_gqa(FAKE, FAKE + 8, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, 0.1, 0, None, None) == -7
+    need = lib.fa_backward_workspace_size(1, 4, 16, 64)
+
+    def bwd(ws=FAKE, ws_bytes=need, dk=FAKE):
+        return lib.fa_backward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dk, FAKE, 1, 4, 2, 16, 64, 0.125, 0,
+                                   None, ws, ws_bytes, None)
+
+    assert bwd(dk=None) == -1
+    assert bwd(ws=None) == -5
+    assert bwd(ws_bytes=need - 1) == -5
+    assert bwd(dk=FAKE + 4) == -7

@@ -30,6 +30,13 @@ REF_MUTATIONS = {
     "dk_wrong_operand": ("dk += scale * (ds.T @ q[rows])", "dk += scale * (ds.T @ k[rows])"),
     "dv_p_not_transposed": ("dv += p.T @ dor", "dv += p @ dor"),
     "dp_uses_k": ("dp = dor @ v.T", "dp = dor @ k.T"),
+    "gqa_interleaved_heads": ("return attention_forward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)",
+                              "return attention_forward(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1))"),
+    "gqa_dk_not_summed": ("return dq, dk.reshape(B, Hkv, G, N, d).sum(axis=2)",
+                          "return dq, dk.reshape(B, Hkv, G, N, d)[:, :, 0]"),
+    "gqa_dv_mean": ("dv.reshape(B, Hkv, G, N, d).sum(axis=2)", "dv.reshape(B, Hkv, G, N, d).mean(axis=2)"),
+    "gqa_dk_summed_over_wrong_axis": ("dk.reshape(B, Hkv, G, N, d).sum(axis=2)",
+                                      "dk.reshape(B, G, Hkv, N, d).sum(axis=1)"),
 }
 
 ONLINE_MUTATIONS = {
