@@ -173,7 +173,9 @@ def run_gpu(args):
     kind, causal = dom
     dom_flops = KERNEL_FLOP_SHARE[kind] * fwd_flops(B, H, N, d, causal)
     achieved = dom_flops / (kms[dom] * 1e-3) / 1e12
-    kname = f"{KERNEL_NAME[kind]}<{d}, {64 if d == 128 else 128}, {'true' if causal else 'false'}, false>"
+    # template arguments: head dim, tile, causal, key padding (and, dK/dV pass, grouped K/V heads)
+    kname = f"{KERNEL_NAME[kind]}<{d}, {64 if d == 128 else 128}, {'true' if causal else 'false'}, false" + (
+        ", false>" if kind == "dkdv" else ">")
     roofline = {
         "bound": "mfma",
         "achieved": round(achieved, 1),
