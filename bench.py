@@ -230,7 +230,8 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
             else:
                 dq = torch.empty_like(t["q"])
                 dk, dv = torch.empty_like(t["k"]), torch.empty_like(t["v"])
-                ws = torch.empty(fa.fa_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+                ws = torch.empty(fa.fa_backward_gqa_workspace_size(B, H, w.kv_heads, N, d), dtype=torch.uint8,
+                                 device=dev)
                 bwd = fa.fa_backward_gqa if grouped else fa.fa_backward
 
                 def call():

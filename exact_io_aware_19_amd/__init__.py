@@ -14,6 +14,7 @@ Low-level calls with the C names (caller allocates every output):
     fa_forward_gqa(q, k, v, o, lse, scale, causal, kv_len=None, stream=None)
     fa_backward_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
                     kv_len=None, stream=None)
+    fa_backward_gqa_workspace_size(B, H, H_kv, N, d)
         grouped K/V heads: k, v, dk, dv are [B, H_kv, N, d] with H_kv dividing H
 
 Convenience wrappers that allocate outputs with torch (grouped K/V heads when k has
@@ -36,6 +37,7 @@ __all__ = [
     "fa_backward_pass",
     "fa_forward_gqa",
     "fa_backward_gqa",
+    "fa_backward_gqa_workspace_size",
     "forward",
     "backward",
     "FAError",
@@ -141,7 +143,7 @@ def fa_forward_gqa(q, k, v, o, lse, scale, causal, kv_len=None, stream=None):
 def fa_backward_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len=None, stream=None):
     """C ``fa_backward_gqa``: k, v, dk, dv are [B, H_kv, N, d]; fills dq, dk, dv in place.
 
-    workspace: a GPU tensor of at least fa_backward_workspace_size(B, H, N, d) bytes.
+    workspace: a GPU tensor of at least fa_backward_gqa_workspace_size(B, H, H_kv, N, d) bytes.
     """
     _check_qkv("q", q)
     shape = tuple(q.shape)
@@ -167,6 +169,11 @@ def fa_backward_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
 def fa_backward_workspace_size(B, H, N, d):
     """C ``fa_backward_workspace_size``."""
     return int(_lib.load().fa_backward_workspace_size(B, H, N, d))
+
+
+def fa_backward_gqa_workspace_size(B, H, H_kv, N, d):
+    """C ``fa_backward_gqa_workspace_size``."""
+    return int(_lib.load().fa_backward_gqa_workspace_size(B, H, H_kv, N, d))
 
 
 def fa_backward(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len=None, stream=None):
@@ -238,9 +245,12 @@ def backward(q, k, v, o, dout, lse, causal=False, scale=None, kv_len=None, works
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
+    grouped = k.dim() == 4 and k.shape[1] != H
     if workspace is None:
-        workspace = torch.empty(fa_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
-    if k.dim() == 4 and k.shape[1] != H:
+        nbytes = (fa_backward_gqa_workspace_size(B, H, int(k.shape[1]), N, d) if grouped
+                  else fa_backward_workspace_size(B, H, N, d))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if grouped:
         fa_backward_gqa(q, k, v, o, dout, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace,
                         kv_len=kv_len)
     else:

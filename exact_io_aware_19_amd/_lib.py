@@ -33,6 +33,7 @@ EXPORTED = (
     "fa_backward_dkdv_pass",
     "fa_forward_gqa",
     "fa_backward_gqa",
+    "fa_backward_gqa_workspace_size",
     "fa_status_string",
 )
 
@@ -68,6 +69,8 @@ def load():
     lib.fa_forward_gqa.restype = i
     lib.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.fa_backward_gqa.restype = i
+    lib.fa_backward_gqa_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_backward_gqa_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -398,7 +398,20 @@ __device__ __forceinline__ void transpose8x8(const unsigned char* nat, uint32_t 
 }
 
 // Store a C fragment holding X^T (rows = head-dim d, column = this lane's row `row`)
-// as bf16 row `row` of a [N][D] matrix, scaled by `mul`.
+// as fp32 row `row` of a [N][D] matrix, scaled by `mul`.
+template <int D>
+__device__ __forceinline__ void store_ct_rows_f32(float* g, int row, const f32x16 (&acc)[D / 32], float mul, int h) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d0 = 32 * db + 8 * gq + 4 * h;
+      const f32x4 out = {acc[db][4 * gq + 0] * mul, acc[db][4 * gq + 1] * mul, acc[db][4 * gq + 2] * mul,
+                         acc[db][4 * gq + 3] * mul};
+      *(f32x4*)(g + (size_t)row * D + d0) = out;
+    }
+}
+// The same as bf16 (round to nearest even).
 template <int D>
 __device__ __forceinline__ void store_ct_rows(uint16_t* g, int row, const f32x16 (&acc)[D / 32], float mul, int h) {
 #pragma unroll

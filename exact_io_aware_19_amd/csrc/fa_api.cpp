@@ -61,10 +61,17 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 // Rows per head in the backward workspace: N rounded up to the dQ pass's 256-row blocks.
 int workspace_rows(int N) { return (N + 255) / 256 * 256; }
 
-size_t workspace_bytes(int B, int H, int N, int d) {
-  (void)d;
-  // D_i and LSE_i * log2(e), fp32 [B][H][nw] each
+size_t stats_bytes(int B, int H, int N) {
+  // D_i and LSE_i * log2(e), fp32 [B][H][nw] each (a multiple of 2 KiB: the partials
+  // that follow stay 256-byte aligned)
   return 2 * (size_t)B * H * workspace_rows(N) * 4;
+}
+
+size_t workspace_bytes(int B, int H, int Hkv, int N, int d) {
+  // grouped K/V heads split over several workgroups: fp32 partial dK and dV per split
+  const int ns = fa355::kv_splits(B, H, Hkv, N);
+  const size_t parts = ns > 1 ? 2 * (size_t)ns * B * Hkv * N * d * 4 : 0;
+  return stats_bytes(B, H, N) + parts;
 }
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -77,7 +84,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   if (st != FA_OK) return st;
   st = check_scale(scale);
   if (st != FA_OK) return st;
-  if (!workspace || ws_bytes < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!workspace || ws_bytes < workspace_bytes(B, H, Hkv, N, d)) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) || ((uintptr_t)workspace & 255u))
     return FA_ERR_ALIGN;
@@ -103,6 +110,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.causal = causal != 0;
+  a.nsplit = fa355::kv_splits(B, H, Hkv, N);
+  a.part = (float*)((char*)workspace + stats_bytes(B, H, N));
   return fa355::launch_backward(a, (hipStream_t)stream, passes) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -127,7 +136,12 @@ int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   if (check_shape(B, H, N, d) != FA_OK) return 0;
-  return workspace_bytes(B, H, N, d);
+  return workspace_bytes(B, H, H, N, d);
+}
+
+size_t fa_backward_gqa_workspace_size(int B, int H, int H_kv, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK || check_kv_heads(H, H_kv) != FA_OK) return 0;
+  return workspace_bytes(B, H, H_kv, N, d);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

@@ -218,6 +218,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kKvBN = kKvWaves * 32;  // key columns per workgroup
+static_assert(kKvBN == kKvBlockKeys, "split planning assumes this many keys per workgroup");
 
 template <int D, int BM>
 struct KvLds {
@@ -309,16 +310,24 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 31, h = l >> 5;
   // one workgroup per (key block, K/V head); with grouped heads it runs the query tiles
   // of every query head of its group in turn and sums their dK, dV in registers
+  // (grouped heads split over nsplit workgroups: workgroup part s runs the group's query
+  // heads [s*G/nsplit, (s+1)*G/nsplit) and writes fp32 partials)
   const int BHkv = p.B * p.Hkv;
+  const int nsplit = GROUPED ? p.nsplit : 1;
   // no mask: each XCD works through whole heads; causal: key block 0 sees the most
   // queries, so it goes first
   const int nkb = (p.N + kKvBN - 1) / kKvBN;
-  int kbi, bhk;
-  block_order<!CAUSAL>((int)blockIdx.x, nkb, BHkv, kbi, bhk);
+  int kbi, hs;
+  block_order<!CAUSAL>((int)blockIdx.x, nkb, BHkv * nsplit, kbi, hs);
+  const int bhk = hs / nsplit, split = hs - bhk * nsplit;
   const int b = bhk / p.Hkv;
   const int N = p.N;
   const int G = GROUPED ? p.H / p.Hkv : 1;          // query heads per K/V head
+  const int g_begin = split * G / nsplit, g_end = (split + 1) * G / nsplit;
   const int bq0 = b * p.H + (bhk - b * p.Hkv) * G;  // first query head of the group
+  // fp32 partials of this workgroup's split (grouped, nsplit > 1)
+  float* const part_dk = GROUPED ? p.part + ((size_t)split * BHkv + bhk) * N * D : nullptr;
+  float* const part_dv = GROUPED ? part_dk + (size_t)nsplit * BHkv * N * D : nullptr;
   const size_t head = (size_t)bhk * N * D;          // K, V, dK, dV
   buf_rsrc qg, dog;
   const float* __restrict__ wl;
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     wl = p.ws_l + (size_t)(bq0 + g) * p.nw;
     wd = p.ws_d + (size_t)(bq0 + g) * p.nw;
   };
-  set_query_head(0);
+  set_query_head(g_begin);
 
   int kv_end = N;
   if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);
@@ -348,8 +357,13 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   }
   if (k0 >= kv_end) {  // every key of this block is padded away: exact zeros
     if (col_store) {
-      store_ct_rows<D>(p.dk + head, kcol, dk, 0.f, h);
-      store_ct_rows<D>(p.dv + head, kcol, dv, 0.f, h);
+      if (nsplit > 1) {
+        store_ct_rows_f32<D>(part_dk, kcol, dk, 0.f, h);
+        store_ct_rows_f32<D>(part_dv, kcol, dv, 0.f, h);
+      } else {
+        store_ct_rows<D>(p.dk + head, kcol, dk, 0.f, h);
+        store_ct_rows<D>(p.dv + head, kcol, dv, 0.f, h);
+      }
     }
     return;
   }
@@ -656,8 +670,8 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     // pipeline; dK, dV keep accumulating.  Causal: every iteration runs masked (exact
     // where no mask is needed), which keeps to two iteration variants.
     constexpr std::integral_constant<bool, CAUSAL> M{};
-    for (int g = 0; g < G; ++g) {
-      if (g > 0) {
+    for (int g = g_begin; g < g_end; ++g) {
+      if (g > g_begin) {
         // the previous head's epilogue has read its last tiles before the copies refill them
         __syncthreads();
         set_query_head(g);
@@ -704,9 +718,40 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   }
   if (col_store) {
     // keys padded away for every query get exact zeros
-    store_ct_rows<D>(p.dk + head, kcol, dk, col_live ? p.scale : 0.f, h);
-    store_ct_rows<D>(p.dv + head, kcol, dv, col_live ? 1.f : 0.f, h);
+    if (nsplit > 1) {
+      store_ct_rows_f32<D>(part_dk, kcol, dk, col_live ? p.scale : 0.f, h);
+      store_ct_rows_f32<D>(part_dv, kcol, dv, col_live ? 1.f : 0.f, h);
+    } else {
+      store_ct_rows<D>(p.dk + head, kcol, dk, col_live ? p.scale : 0.f, h);
+      store_ct_rows<D>(p.dv + head, kcol, dv, col_live ? 1.f : 0.f, h);
+    }
   }
+}
+
+// --------------------------------------------------------------------------------------
+// launch 3 (grouped K/V heads split over several workgroups only): dK, dV = the sum of
+// the nsplit fp32 partials, in split order (deterministic), rounded to bf16.  Eight
+// consecutive elements per thread; the element count is a multiple of 8 (d is).
+// --------------------------------------------------------------------------------------
+constexpr int kReduceThreads = 256;
+
+__global__ __launch_bounds__(kReduceThreads) void fa_bwd_kv_reduce_kernel(const float* __restrict__ part,
+                                                                         uint16_t* __restrict__ dk,
+                                                                         uint16_t* __restrict__ dv, size_t n,
+                                                                         int nsplit) {
+  const size_t e = ((size_t)blockIdx.x * kReduceThreads + threadIdx.x) * 8;  // over [dK | dV]
+  if (e >= 2 * n) return;
+  const bool is_v = e >= n;
+  const size_t off = is_v ? e - n : e;
+  const float* src = part + (is_v ? (size_t)nsplit * n : 0) + off;
+  f32x4 a = *(const f32x4*)src, b4 = *(const f32x4*)(src + 4);
+  for (int s = 1; s < nsplit; ++s) {
+    a += *(const f32x4*)(src + (size_t)s * n);
+    b4 += *(const f32x4*)(src + (size_t)s * n + 4);
+  }
+  const u32x4 out = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b4[0], b4[1]),
+                     pack_bf16x2(b4[2], b4[3])};
+  *(u32x4*)((is_v ? dv : dk) + off) = out;
 }
 
 // --------------------------------------------------------------------------------------
@@ -730,12 +775,20 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int passes) {
   }
   if (passes & 2) {
     constexpr size_t lds = KvLds<D, BM>::BYTES;
-    auto kern = a.Hkv != a.H ? fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN, true>
-                             : fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN, false>;
+    const bool grouped = a.Hkv != a.H;
+    auto kern = grouped ? fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN, true>
+                        : fa_bwd_dkdv_kernel<D, BM, CAUSAL, KVLEN, false>;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)((a.N + kKvBN - 1) / kKvBN) * (unsigned)(a.B * a.Hkv);
+    const int nsplit = grouped ? a.nsplit : 1;
+    const unsigned grid = (unsigned)((a.N + kKvBN - 1) / kKvBN) * (unsigned)(a.B * a.Hkv * nsplit);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), lds, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || nsplit == 1) return e;
+    const size_t n = (size_t)a.B * a.Hkv * a.N * D;
+    const unsigned rgrid = (unsigned)((2 * n / 8 + kReduceThreads - 1) / kReduceThreads);
+    hipLaunchKernelGGL(fa_bwd_kv_reduce_kernel, dim3(rgrid), dim3(kReduceThreads), 0, stream, a.part, a.dk, a.dv, n,
+                       nsplit);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -39,7 +39,27 @@ struct BwdArgs {
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   int causal;
+  // grouped K/V heads with nsplit > 1: the query heads of a group are split over nsplit
+  // workgroups per key block, which write fp32 partial dK, dV ([nsplit][B*Hkv][N][d]
+  // each, dV right after dK) summed in a fixed order by a second kernel
+  int nsplit;
+  float* part;
 };
+
+// Key columns per dK/dV workgroup.
+constexpr int kKvBlockKeys = 128;
+// Workgroups a dK/dV launch aims for (two per CU); fewer key blocks x K/V heads than this
+// split each group's query heads over several workgroups.
+constexpr int kKvTargetBlocks = 512;
+
+// Number of workgroups that share the query heads of one (key block, K/V head).
+inline int kv_splits(int B, int H, int Hkv, int N) {
+  if (Hkv >= H) return 1;
+  const long long base = (long long)((N + kKvBlockKeys - 1) / kKvBlockKeys) * B * Hkv;
+  const long long want = (kKvTargetBlocks + base - 1) / base;
+  const int G = H / Hkv;
+  return (int)(want < 1 ? 1 : (want > G ? G : want));
+}
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 // passes: bit 0 = dQ pass (dq + row statistics), bit 1 = dK/dV pass

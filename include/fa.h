@@ -134,13 +134,24 @@ int fa_backward_dkdv_pass(const void* q, const void* k, const void* v, const voi
  * sums over the group of the per-query-head gradients.
  *   q, o, dout, dq: [B][H][N][d];  k, v, dk, dv: [B][H_kv][N][d];  lse: [B][H][N].
  * kv_len: device int32[B] or NULL for no padding.  Everything else (masks, scale,
- * alignment, workspace of fa_backward_workspace_size(B, H, N, d) bytes, ownership and
- * errors) is as in fa_forward_kvlen / fa_backward_kvlen; H_kv < 1 or H % H_kv != 0
- * returns FA_ERR_KVHEADS.  The backward is deterministic: each K/V head's dk and dv
- * accumulate its group's query heads in a fixed order, in registers.
+ * alignment, ownership and errors) is as in fa_forward_kvlen / fa_backward_kvlen, except
+ * that the backward's workspace must hold fa_backward_gqa_workspace_size(B, H, H_kv, N,
+ * d) bytes; H_kv < 1 or H % H_kv != 0 returns FA_ERR_KVHEADS.  The backward is
+ * deterministic: each K/V head's dk and dv accumulate its group's query heads in a
+ * fixed order (in registers, and across workgroups through fp32 partials summed in
+ * split order).
  */
 int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
                    int d, float scale, int causal, const int32_t* kv_len, fa_stream_t stream);
+/*
+ * Workspace bytes fa_backward_gqa needs: the row statistics of fa_backward_workspace_size
+ * (B, H, N, d), plus, when the B * H_kv * ceil(N / 128) (key block, K/V head) pairs are
+ * too few to fill the GPU, fp32 partial dK and dV for each of the S workgroups that split
+ * a group's query heads (2 * S * B * H_kv * N * d * 4 bytes, S <= H / H_kv); the partials
+ * are summed in a fixed order, so results stay deterministic.  Equals
+ * fa_backward_workspace_size(B, H, N, d) when H_kv = H.  Returns 0 for invalid sizes.
+ */
+size_t fa_backward_gqa_workspace_size(int B, int H, int H_kv, int N, int d);
 int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                     void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
                     const int32_t* kv_len, void* workspace, size_t workspace_bytes, fa_stream_t stream);

@@ -134,7 +134,7 @@ def test_gqa_entry_points_validate_like_the_others(lib):
     assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 96, 0.125, 0, None, None) == -3
     assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, 0.0, 0, None, None) == -4
     assert lib.fa_forward_gqa(FAKE, FAKE + 8, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, 0.1, 0, None, None) == -7
-    need = lib.fa_backward_workspace_size(1, 4, 16, 64)
+    need = lib.fa_backward_gqa_workspace_size(1, 4, 2, 16, 64)
 
     def bwd(ws=FAKE, ws_bytes=need, dk=FAKE):
         return lib.fa_backward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dk, FAKE, 1, 4, 2, 16, 64, 0.125, 0,
@@ -144,3 +144,20 @@ def test_gqa_entry_points_validate_like_the_others(lib):
     assert bwd(ws=None) == -5
     assert bwd(ws_bytes=need - 1) == -5
     assert bwd(dk=FAKE + 4) == -7
+
+
+def test_gqa_workspace_size(lib):
+    B, H, N, d = 2, 16, 4096, 128
+    stats = 2 * 4 * B * H * ((N + 255) // 256 * 256)
+    # enough (key block, K/V head) pairs: statistics only, like the ungrouped size
+    assert lib.fa_backward_gqa_workspace_size(B, H, H, N, d) == lib.fa_backward_workspace_size(B, H, N, d) == stats
+    assert lib.fa_backward_gqa_workspace_size(4, H, 8, N, d) == 2 * 4 * 4 * H * ((N + 255) // 256 * 256)
+    # MQA at B=2: 64 pairs < 512 workgroups -> 8 splits, fp32 partial dK and dV each
+    assert lib.fa_backward_gqa_workspace_size(B, H, 1, N, d) == stats + 2 * 8 * B * 1 * N * d * 4
+    # never more splits than query heads per group
+    assert lib.fa_backward_gqa_workspace_size(1, 2, 1, 128, 64) == 2 * 4 * 2 * 256 + 2 * 2 * 1 * 128 * 64 * 4
+    assert lib.fa_backward_gqa_workspace_size(B, H, 3, N, d) == 0
+    assert lib.fa_backward_gqa_workspace_size(B, H, 1, N, 80) == 0
+    need = lib.fa_backward_gqa_workspace_size(1, 2, 1, 128, 64)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 128, 64, 0.125, 0, None, FAKE)
+    assert lib.fa_backward_gqa(*args, need - 1, None) == -5
