@@ -150,45 +150,115 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
     if (kt0 < wave_kend) {
       bool need_mask = kt0 + BN > kv_end;
       if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > q0 + w * 32);
-      // no running statistics in the backward: each 32-key block is finished on its own
+      // No running statistics in the backward: each 32-key block is finished on its own.
+      // Pairs of key blocks (a, b) run as one pinned stream of products with operand
+      // fragments read kLook products ahead:
+      //   S, dP (a) | S, dP (b) with P, dS (a) between the products | dQ (a) with P, dS (b)
+      //   between them | dQ (b)
+      // so the elementwise work of one block overlaps the other block's products.
+      auto pair = [&](auto MASK, auto kbp_c) {
+        constexpr int KA = 2 * decltype(kbp_c)::value;
+        constexpr int NSP = 2 * NKK, NQ = 2 * NDB, T = 2 * NSP + 2 * NQ;
+        constexpr int kLook = 2;
+        f32x16 sc[2], dp[2];
+        u32x4 dsk[2][2];
+        // op t: [0, NSP) S/dP of a, [NSP, 2NSP) S/dP of b, then dQ of a, dQ of b
+        auto aread = [&](int t) -> u32x4 {
+          if (t < 2 * NSP) {
+            const int kb = KA + t / NSP, r = t % NSP, kk = r >> 1;
+            return lds_read128((r & 1) ? vbuf(cur) : kbuf(cur), nb[kk & 1] + kb * 2 * BLK16 + (kk >> 1) * 64 * 16);
+          }
+          const int u = t - 2 * NSP, kb = KA + u / NQ, m = u % NQ, sb = m / NDB, db = m % NDB;
+          const uint32_t off = (2 * kb + sb) * BLK16 + db * 4 * 16 * 16;
+          const u32x2 a0 = lds_read_tr16(kbuf(cur), trb + off), a1 = lds_read_tr16(kbuf(cur), (trb ^ 64u) + off);
+          return u32x4{a0[0], a0[1], a1[0], a1[1]};
+        };
+        // P, dS for rows 2e, 2e+1 of half sb of block x of the pair
+        auto group = [&](int x, int g) {
+          const int sb = g >> 2, e = g & 3, r0 = 8 * sb + 2 * e;
+          float s0 = sc[x][r0], s1 = sc[x][r0 + 1];
+          if constexpr (decltype(MASK)::value) {
+            const int key0 = kt0 + 32 * (KA + x) + c_row(r0, h);
+            bool bad0 = key0 >= kv_end, bad1 = key0 + 1 >= kv_end;
+            if constexpr (CAUSAL) {
+              bad0 = bad0 || key0 > qrow;
+              bad1 = bad1 || key0 + 1 > qrow;
+            }
+            s0 = bad0 ? -INFINITY : s0;
+            s1 = bad1 ? -INFINITY : s1;
+          }
+          const float p0 = fast_exp2(__builtin_fmaf(s0, sl, -lse2));
+          const float p1 = fast_exp2(__builtin_fmaf(s1, sl, -lse2));
+          dsk[x][sb][e] = pack_bf16x2(p0 * (dp[x][r0] - di), p1 * (dp[x][r0 + 1] - di));
+        };
+        u32x4 fr[kLook];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        for (int t = 0; t < kLook; ++t) fr[t] = aread(t);
+        static_for<T>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          const u32x4 a = fr[t % kLook];
+          if constexpr (t + kLook < T) fr[t % kLook] = aread(t + kLook);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (t < 2 * NSP) {
+            constexpr int x = t / NSP, r = t % NSP, kk = r >> 1;
+            if constexpr (r & 1) dp[x] = mfma32(a, dof[kk], kk == 0 ? f32x16{} : dp[x]);
+            else sc[x] = mfma32(a, qf[kk], kk == 0 ? f32x16{} : sc[x]);
+            // P, dS of block a: its eight groups spread over the dP products of block b
+            if constexpr (x == 1 && (r & 1)) {
+              constexpr int G0 = (8 * kk) / NKK, G1 = (8 * (kk + 1)) / NKK;
+              static_for<G1 - G0>([&](auto gc) { group(0, G0 + decltype(gc)::value); });
+            }
+          } else {
+            constexpr int u = t - 2 * NSP, x = u / NQ, m = u % NQ, sb = m / NDB, db = m % NDB;
+            dq[db] = mfma32(a, dsk[x][sb], dq[db]);
+            // P, dS of block b: spread over the dQ products of block a
+            if constexpr (x == 0) {
+              constexpr int G0 = (8 * m) / NQ, G1 = (8 * (m + 1)) / NQ;
+              static_for<G1 - G0>([&](auto gc) { group(1, G0 + decltype(gc)::value); });
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      static_assert(NKB % 2 == 0, "key blocks run in pairs");
+      if (!need_mask) {
+        static_for<NKB / 2>([&](auto kbp) { pair(std::false_type{}, kbp); });
+      } else {
+        // edge tiles (causal diagonal, padding, ragged end): one block at a time
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const uint32_t off = nb[kk & 1] + kb * 2 * BLK16 + (kk >> 1) * 64 * 16;
-          const u32x4 ak = lds_read128(kbuf(cur), off);
-          s = mfma32(ak, qf[kk], s);
-          const u32x4 av = lds_read128(vbuf(cur), off);
-          dp = mfma32(av, dof[kk], dp);
+        for (int kb = 0; kb < NKB; ++kb) {
+          f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            const uint32_t off = nb[kk & 1] + kb * 2 * BLK16 + (kk >> 1) * 64 * 16;
+            s = mfma32(lds_read128(kbuf(cur), off), qf[kk], s);
+            dp = mfma32(lds_read128(vbuf(cur), off), dof[kk], dp);
+          }
+          u32x4 dsk[2];
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r0 = 8 * sb + 2 * e;
+              const int key0 = kt0 + 32 * kb + c_row(r0, h);
+              bool bad0 = key0 >= kv_end, bad1 = key0 + 1 >= kv_end;
+              if constexpr (CAUSAL) {
+                bad0 = bad0 || key0 > qrow;
+                bad1 = bad1 || key0 + 1 > qrow;
+              }
+              const float p0 = bad0 ? 0.f : fast_exp2(__builtin_fmaf(s[r0], sl, -lse2));
+              const float p1 = bad1 ? 0.f : fast_exp2(__builtin_fmaf(s[r0 + 1], sl, -lse2));
+              dsk[sb][e] = pack_bf16x2(p0 * (dp[r0] - di), p1 * (dp[r0 + 1] - di));
+            }
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const uint32_t off = (2 * kb + sb) * BLK16 + db * 4 * 16 * 16;
+              const u32x2 a0 = lds_read_tr16(kbuf(cur), trb + off), a1 = lds_read_tr16(kbuf(cur), (trb ^ 64u) + off);
+              dq[db] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, dsk[sb], dq[db]);
+            }
         }
-        if (need_mask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + 32 * kb + c_row(r, h);
-            bool bad = key >= kv_end;
-            if constexpr (CAUSAL) bad = bad || key > qrow;
-            if (bad) s[r] = -INFINITY;
-          }
-        }
-        u32x4 dsk[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r0 = 8 * sb + 2 * i;
-            const float p0 = fast_exp2(__builtin_fmaf(s[r0], sl, -lse2));
-            const float p1 = fast_exp2(__builtin_fmaf(s[r0 + 1], sl, -lse2));
-            dsk[sb][i] = pack_bf16x2(p0 * (dp[r0] - di), p1 * (dp[r0 + 1] - di));
-          }
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const uint32_t off = (2 * kb + sb) * BLK16 + db * 4 * 16 * 16;
-            const u32x2 a0 = lds_read_tr16(kbuf(cur), trb + off), a1 = lds_read_tr16(kbuf(cur), (trb ^ 64u) + off);
-            dq[db] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, dsk[sb], dq[db]);
-          }
       }
     }
     wait_vmem();
