@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
       //   S, dP (a) | S, dP (b) with P, dS (a) between the products | dQ (a) with P, dS (b)
       //   between them | dQ (b)
       // so the elementwise work of one block overlaps the other block's products.
-      auto pair = [&](auto MASK, auto kbp_c) {
+      auto pair = [&](auto kbp_c) {  // interior tiles only: no mask
         constexpr int KA = 2 * decltype(kbp_c)::value;
         constexpr int NSP = 2 * NKK, NQ = 2 * NDB, T = 2 * NSP + 2 * NQ;
         constexpr int kLook = 2;
@@ -176,19 +176,8 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
         // P, dS for rows 2e, 2e+1 of half sb of block x of the pair
         auto group = [&](int x, int g) {
           const int sb = g >> 2, e = g & 3, r0 = 8 * sb + 2 * e;
-          float s0 = sc[x][r0], s1 = sc[x][r0 + 1];
-          if constexpr (decltype(MASK)::value) {
-            const int key0 = kt0 + 32 * (KA + x) + c_row(r0, h);
-            bool bad0 = key0 >= kv_end, bad1 = key0 + 1 >= kv_end;
-            if constexpr (CAUSAL) {
-              bad0 = bad0 || key0 > qrow;
-              bad1 = bad1 || key0 + 1 > qrow;
-            }
-            s0 = bad0 ? -INFINITY : s0;
-            s1 = bad1 ? -INFINITY : s1;
-          }
-          const float p0 = fast_exp2(__builtin_fmaf(s0, sl, -lse2));
-          const float p1 = fast_exp2(__builtin_fmaf(s1, sl, -lse2));
+          const float p0 = fast_exp2(__builtin_fmaf(sc[x][r0], sl, -lse2));
+          const float p1 = fast_exp2(__builtin_fmaf(sc[x][r0 + 1], sl, -lse2));
           dsk[x][sb][e] = pack_bf16x2(p0 * (dp[x][r0] - di), p1 * (dp[x][r0 + 1] - di));
         };
         u32x4 fr[kLook];
@@ -222,7 +211,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
       };
       static_assert(NKB % 2 == 0, "key blocks run in pairs");
       if (!need_mask) {
-        static_for<NKB / 2>([&](auto kbp) { pair(std::false_type{}, kbp); });
+        static_for<NKB / 2>([&](auto kbp) { pair(kbp); });
       } else {
         // edge tiles (causal diagonal, padding, ragged end): one block at a time
 #pragma unroll
