@@ -505,10 +505,10 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   //     last block on the first block of the next iteration), so that every product
   //     slot carries about the same amount of VALU work; each group runs in three
   //     stages on consecutive products (placement in KvSched);
-  //   - the direct copies of tile i+2 (every fourth product from 2: a burst of copies
+  //   - the direct copies of tile i+2 (every fifth product from 2: a burst of copies
   //     stalls instruction issue; early enough that their latency hides behind the
   //     iteration) and the transposition of tile i+1 (reads
-  //     on products 0-7, one 8-row output on every third product from 8).
+  //     on products 0-7, one 8-row output on every seventh product from 8).
   // P, dS live in two register sets (tile being reduced / tile being scored) whose
   // roles swap every iteration; iterations run in pairs so the set index is a
   // compile-time constant and no register copies are needed.  S, dP are double
@@ -516,7 +516,10 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   constexpr int NS = 2 * NKK, NR = 4 * NDB, NSTEP = NS + NR, T = NQB * NSTEP;
   constexpr int kLook = 4;
   static_assert(NQB % 2 == 0, "S, dP buffers alternate by block parity");
-  static_assert(8 + 3 * 7 < T && 2 + 4 * (NDMA - 1) < T, "extra work must fit in the stream");
+  // side work spacing (measured): copies every kDmaStep products from 2, transposition
+  // writes every kTxStep products from 8
+  constexpr int kDmaStep = 5, kTxStep = 7;
+  static_assert(8 + kTxStep * 7 < T && 2 + kDmaStep * (NDMA - 1) < T, "extra work must fit in the stream");
   u32x4 ps[2][NQB][2], dss[2][NQB][2];  // P, dS as bf16 pairs: [set][block][16-row half]
   f32x16 sbuf[2], dbuf[2];              // S, dP by block parity
 
@@ -618,8 +621,8 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
       const u32x4 a = fr[t % kLook];
       if constexpr (t + kLook < T) fr[t % kLook] = aread(t + kLook);
       if constexpr (t < 8) tx[t] = lds_read128(t_src, t_rd ^ (16u * t));
-      if constexpr (t >= 8 && (t - 8) % 3 == 0 && (t - 8) / 3 < 8) {
-        constexpr int jj = (t - 8) / 3;
+      if constexpr (t >= 8 && (t - 8) % kTxStep == 0 && (t - 8) / kTxStep < 8) {
+        constexpr int jj = (t - 8) / kTxStep;
         u32x4 y;
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp)
@@ -627,7 +630,8 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
                            : lo16_pair(tx[2 * pp][jj >> 1], tx[2 * pp + 1][jj >> 1]);
         lds_write128(t_dst, t_wr ^ (16u * jj), y);
       }
-      if constexpr (t >= 2 && (t - 2) % 4 == 0 && (t - 2) / 4 < NDMA) dma_item((t - 2) / 4, it2, cs);
+      if constexpr (t >= 2 && (t - 2) % kDmaStep == 0 && (t - 2) / kDmaStep < NDMA)
+        dma_item((t - 2) / kDmaStep, it2, cs);
       if constexpr (t + 2 < T && Sch::unit_at(t + 2) >= 0)
         stat_read(std::integral_constant<int, t + 2>{}, sl2, sd2);
       // first read of block q's S, dP by VALU code: the products are inline assembly,
