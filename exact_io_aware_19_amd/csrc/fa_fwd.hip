@@ -221,8 +221,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
       constexpr bool CPK = decltype(cpk)::value;
       auto side = [&](auto ic, auto mc) {
         constexpr int i = decltype(ic)::value, SP = decltype(mc)::value / 16;
-        if constexpr (i % (2 * SP) == SP % 2 && i / (2 * SP) < 4) vh.store(vnext, i / (2 * SP));  // V^T columns
-        if constexpr (CPK && i % (4 * SP) == 2 && i / (4 * SP) < KCOPY) k_copy(krow, knext, i / (4 * SP));
+        // placement (measured): the V^T column stores late in a full stream (products
+        // 24, 26, 28, 30 of 32), the K copies one every four products from 2
+        constexpr int V0 = SP == 2 ? 24 : 1, K0 = 2;
+        if constexpr (i >= V0 && (i - V0) % 2 == 0 && (i - V0) / 2 < 4) vh.store(vnext, (i - V0) / 2);
+        if constexpr (CPK && i >= K0 && (i - K0) % 4 == 0 && (i - K0) / 4 < KCOPY) k_copy(krow, knext, (i - K0) / 4);
       };
       if (do_pv && do_s) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV + NS>{}, vb_, kt, side);
       else if (do_pv) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV>{}, vb_, kt, side);
