@@ -13,7 +13,9 @@ bf16 (round to nearest, ties to even).
 Draw order per workload (one generator per workload seed): q ([B, H, N, d] float32),
 k, v ([B, H_kv, N, d]; H_kv = H unless the workload groups its K/V heads), then dO,
 then the key-padding lengths, then the indices of the key rows scaled x8, then the
-sampled query rows.
+sampled query rows, then (workloads with outliers) the flat indices of the q entries and
+of the k entries multiplied by 16.  The +-1 sign vector of the FP8 path's incoherent
+processing comes from its own generator (``fp8_signs``).
 """
 
 from dataclasses import dataclass, field
@@ -28,6 +30,7 @@ __all__ = [
     "f32_to_bf16_bits",
     "bf16_bits_to_f64",
     "generate",
+    "fp8_signs",
 ]
 
 
@@ -47,6 +50,7 @@ class Workload:
     backward: bool = True
     note: str = ""
     h_kv: int = 0                  # K/V heads (grouped-query attention); 0 = H
+    outlier_frac: float = 0.0      # fraction of the entries of q and k multiplied by 16 (FP8 workloads)
 
     @property
     def shape(self):
@@ -83,9 +87,19 @@ WORKLOADS = {
                          note="long-context causal forward; 1% of key rows x8; 64 sampled query rows"),
     "gqa_n8192": Workload("gqa_n8192", 2, 16, 8192, 128, True, 1.0 / math.sqrt(128), 1006, h_kv=4,
                           note="grouped K/V heads (4 query heads per K/V head), causal, large-head shape"),
+    "fp8_outlier": Workload("fp8_outlier", 1, 4, 1000, 128, False, 1.0 / math.sqrt(128), 1008, backward=False,
+                            outlier_frac=0.001,
+                            note="FP8 forward accuracy: N(0,1) with 0.1% of the q and k entries x16, ragged N"),
     "mqa_n4096": Workload("mqa_n4096", 2, 16, 4096, 128, False, 1.0 / math.sqrt(128), 1007, h_kv=1,
                           note="multi-query attention (one K/V head), large-head shape"),
 }
+
+
+def fp8_signs(d, seed):
+    """The +-1 vector (float32 [d]) of the FP8 path's incoherent processing, drawn from
+    its own PCG64 generator (seed + 7919) so that it does not disturb any input draw."""
+    rng = np.random.default_rng(seed + 7919)
+    return np.where(rng.integers(0, 2, size=d) == 1, 1.0, -1.0).astype(np.float32)
 
 
 def get_workload(name):
@@ -172,6 +186,10 @@ def generate(w, with_do=None, shape_override=None):
     rows = None
     if w.sampled_rows:
         rows = np.sort(rng.choice(N, size=min(w.sampled_rows, N), replace=False))
+    if w.outlier_frac > 0:
+        for t in (qf, kf):
+            idx = rng.choice(t.size, size=max(1, int(w.outlier_frac * t.size)), replace=False)
+            t.reshape(-1)[idx] *= 16.0  # exact in bf16
     return Inputs(
         workload=w,
         q=f32_to_bf16_bits(qf),

@@ -3,4 +3,4 @@
 Only the test suite, the smoke check and the bench's CPU-baseline leg may import this
 package.  It shares no code with the HIP path and never touches a GPU.
 """
-from . import ref, online  # noqa: F401
+from . import ref, online, fp8  # noqa: F401
