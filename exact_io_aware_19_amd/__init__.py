@@ -17,6 +17,16 @@ Low-level calls with the C names (caller allocates every output):
     fa_backward_gqa_workspace_size(B, H, H_kv, N, d)
         grouped K/V heads: k, v, dk, dv are [B, H_kv, N, d] with H_kv dividing H
 
+FP8 forward (block quantisation + incoherent processing; OCP E4M3 codes as uint8):
+    fa_fp8_quantize_qk(x, x8, scales, signs=None, post_scale=1.0, stream=None)
+        x bf16 [B, H, N, d] -> x8 uint8 [B, H, N, d], scales fp32 [B, H, ceil(N/64)]
+    fa_fp8_quantize_v(v, v8t, scales, stream=None)
+        v bf16 [B, H, N, d] -> v8t uint8 [B, H, ceil(N/64), d, 64] (transposed tiles in
+        the key order of the P V product), scales fp32 [B, H, d]
+    fa_forward_fp8(q8, sq, k8, sk, v8t, sv, o, lse, scale, causal, kv_len=None, stream=None)
+    fp8_v8t_to_rows(v8t, N): the codes of fa_fp8_quantize_v back in [B, H, N, d] order
+    forward_fp8(q, k, v, causal=False, scale=None, kv_len=None, signs=None) -> (o, lse)
+
 Convenience wrappers that allocate outputs with torch (grouped K/V heads when k has
 fewer heads than q):
     forward(q, k, v, causal=False, scale=None, kv_len=None) -> (o, lse)
@@ -38,6 +48,11 @@ __all__ = [
     "fa_forward_gqa",
     "fa_backward_gqa",
     "fa_backward_gqa_workspace_size",
+    "fa_fp8_quantize_qk",
+    "fa_fp8_quantize_v",
+    "fa_forward_fp8",
+    "fp8_v8t_to_rows",
+    "forward_fp8",
     "forward",
     "backward",
     "FAError",
@@ -256,3 +271,101 @@ def backward(q, k, v, o, dout, lse, causal=False, scale=None, kv_len=None, works
     else:
         fa_backward(q, k, v, o, dout, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace, kv_len=kv_len)
     return dq, dk, dv
+
+
+# ---- FP8 forward ---------------------------------------------------------------------
+FP8_BLOCK = 64  # rows per Q/K scale block, keys per V^T tile
+
+
+def _check_dev(name, t, dtype, shape):
+    torch = _torch()
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def fa_fp8_quantize_qk(x, x8, scales, signs=None, post_scale=1.0, stream=None):
+    """C ``fa_fp8_quantize_qk``: fills x8 (E4M3 codes, uint8) and the 64-row block scales."""
+    torch = _torch()
+    _check_qkv("x", x)
+    B, H, N, d = x.shape
+    _check_dev("x8", x8, torch.uint8, (B, H, N, d))
+    _check_dev("scales", scales, torch.float32, (B, H, -(-N // FP8_BLOCK)))
+    sp_ = None
+    if signs is not None:
+        _check_dev("signs", signs, torch.float32, (d,))
+        sp_ = signs.data_ptr()
+    st = _lib.load().fa_fp8_quantize_qk(x.data_ptr(), x8.data_ptr(), scales.data_ptr(), sp_, float(post_scale),
+                                        B, H, N, d, _stream_ptr(stream, x.device))
+    _lib.check(st, "fa_fp8_quantize_qk")
+
+
+def fa_fp8_quantize_v(v, v8t, scales, stream=None):
+    """C ``fa_fp8_quantize_v``: fills v8t (transposed E4M3 tiles) and the column scales."""
+    torch = _torch()
+    _check_qkv("v", v)
+    B, H, N, d = v.shape
+    _check_dev("v8t", v8t, torch.uint8, (B, H, -(-N // FP8_BLOCK), d, FP8_BLOCK))
+    _check_dev("scales", scales, torch.float32, (B, H, d))
+    st = _lib.load().fa_fp8_quantize_v(v.data_ptr(), v8t.data_ptr(), scales.data_ptr(), B, H, N, d,
+                                       _stream_ptr(stream, v.device))
+    _lib.check(st, "fa_fp8_quantize_v")
+
+
+def fa_forward_fp8(q8, sq, k8, sk, v8t, sv, o, lse, scale, causal, kv_len=None, stream=None):
+    """C ``fa_forward_fp8``: fills o (bf16) and lse (fp32) in place."""
+    torch = _torch()
+    _check_qkv("o", o)
+    B, H, N, d = o.shape
+    nb = -(-N // FP8_BLOCK)
+    for name, t in (("q8", q8), ("k8", k8)):
+        _check_dev(name, t, torch.uint8, (B, H, N, d))
+    _check_dev("v8t", v8t, torch.uint8, (B, H, nb, d, FP8_BLOCK))
+    for name, t in (("q_scale", sq), ("k_scale", sk)):
+        _check_dev(name, t, torch.float32, (B, H, nb))
+    _check_dev("v_scale", sv, torch.float32, (B, H, d))
+    _check_lse(lse, (B, H, N, d))
+    st = _lib.load().fa_forward_fp8(q8.data_ptr(), sq.data_ptr(), k8.data_ptr(), sk.data_ptr(), v8t.data_ptr(),
+                                    sv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                                    int(bool(causal)), _kv_ptr(kv_len, B, o.device), _stream_ptr(stream, o.device))
+    _lib.check(st, "fa_forward_fp8")
+
+
+def fp8_v8t_to_rows(v8t, N):
+    """Codes of ``fa_fp8_quantize_v`` in natural [B, H, N, d] order (index bookkeeping of
+    the documented layout only): byte 32*g + p of row c of tile t is V[64 t + key(g, p)][c]
+    with key(g, p) = 32*(p//16) + 8*((p%16)//4) + 4*g + p%4."""
+    torch = _torch()
+    B, H, nb, d, _ = v8t.shape
+    pos = torch.arange(FP8_BLOCK)
+    g, p = pos // 32, pos % 32
+    key = 32 * (p // 16) + 8 * ((p % 16) // 4) + 4 * g + p % 4
+    inv = torch.empty_like(key)
+    inv[key] = pos
+    rows = v8t.permute(0, 1, 2, 4, 3)[:, :, :, inv.to(v8t.device), :]  # [B, H, nb, 64 keys, d]
+    return rows.reshape(B, H, nb * FP8_BLOCK, d)[:, :, :N].contiguous()
+
+
+def forward_fp8(q, k, v, causal=False, scale=None, kv_len=None, signs=None):
+    """Quantise q, k, v (bf16) and run the FP8 forward; signs (fp32 [d] of +-1 on the GPU)
+    turns on incoherent processing.  Returns (o, lse)."""
+    torch = _torch()
+    _check_qkv("q", q)
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _check_qkv(name, t, q.shape)
+    nb = -(-N // FP8_BLOCK)
+    dev = q.device
+    q8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=dev)
+    k8 = torch.empty_like(q8)
+    v8t = torch.empty((B, H, nb, d, FP8_BLOCK), dtype=torch.uint8, device=dev)
+    sq = torch.empty((B, H, nb), dtype=torch.float32, device=dev)
+    sk = torch.empty_like(sq)
+    sv = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    fa_fp8_quantize_qk(q, q8, sq, signs, 1.0 / d if signs is not None else 1.0)
+    fa_fp8_quantize_qk(k, k8, sk, signs, 1.0)
+    fa_fp8_quantize_v(v, v8t, sv)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    fa_forward_fp8(q8, sq, k8, sk, v8t, sv, o, lse, _default_scale(d, scale), causal, kv_len=kv_len)
+    return o, lse

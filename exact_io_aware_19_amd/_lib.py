@@ -34,6 +34,9 @@ EXPORTED = (
     "fa_forward_gqa",
     "fa_backward_gqa",
     "fa_backward_gqa_workspace_size",
+    "fa_fp8_quantize_qk",
+    "fa_fp8_quantize_v",
+    "fa_forward_fp8",
     "fa_status_string",
 )
 
@@ -71,6 +74,12 @@ def load():
     lib.fa_backward_gqa.restype = i
     lib.fa_backward_gqa_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_backward_gqa_workspace_size.restype = sz
+    lib.fa_fp8_quantize_qk.argtypes = [vp, vp, vp, vp, f, i, i, i, i, vp]
+    lib.fa_fp8_quantize_qk.restype = i
+    lib.fa_fp8_quantize_v.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib.fa_fp8_quantize_v.restype = i
+    lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    lib.fa_forward_fp8.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -21,7 +21,7 @@ LIB_NAME = "libfa355.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_api.cpp"]
 
 COMMON_FLAGS = [
     "-O3",

@@ -181,6 +181,59 @@ int fa_backward_dkdv_pass(const void* q, const void* k, const void* v, const voi
                        workspace_bytes_, stream, 2);
 }
 
+int fa_fp8_quantize_qk(const void* x, uint8_t* x8, float* scales, const float* signs, float post_scale, int B, int H,
+                       int N, int d, fa_stream_t stream) {
+  if (!x || !x8 || !scales) return FA_ERR_NULL;
+  const int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!isfinite(post_scale) || !(post_scale > 0.f)) return FA_ERR_SCALE;
+  if (!aligned16(x) || !aligned16(x8) || ((uintptr_t)scales & 3u) || ((uintptr_t)signs & 3u)) return FA_ERR_ALIGN;
+  return fa355::launch_fp8_quantize_rows((const uint16_t*)x, x8, scales, signs, post_scale, B, H, N, d,
+                                         (hipStream_t)stream) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
+}
+
+int fa_fp8_quantize_v(const void* v, uint8_t* v8t, float* scales, int B, int H, int N, int d, fa_stream_t stream) {
+  if (!v || !v8t || !scales) return FA_ERR_NULL;
+  const int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(v) || !aligned16(v8t) || ((uintptr_t)scales & 3u)) return FA_ERR_ALIGN;
+  return fa355::launch_fp8_quantize_v((const uint16_t*)v, v8t, scales, B, H, N, d, (hipStream_t)stream) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
+}
+
+int fa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                   const uint8_t* v8t, const float* v_scale, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !v8t || !v_scale || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) || ((uintptr_t)lse & 3u) ||
+      ((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+    return FA_ERR_ALIGN;
+  fa355::Fp8FwdArgs a;
+  a.q8 = q8;
+  a.sq = q_scale;
+  a.k8 = k8;
+  a.sk = k_scale;
+  a.v8t = v8t;
+  a.sv = v_scale;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.kv_len = kv_len;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal != 0;
+  return fa355::launch_forward_fp8(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";

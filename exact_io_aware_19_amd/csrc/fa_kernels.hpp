@@ -61,7 +61,27 @@ inline int kv_splits(int B, int H, int Hkv, int N) {
   return (int)(want < 1 ? 1 : (want > G ? G : want));
 }
 
+struct Fp8FwdArgs {
+  const uint8_t* q8;   // E4M3 codes [B][H][N][d]
+  const float* sq;     // Q block scales [B][H][ceil(N/64)]
+  const uint8_t* k8;   // E4M3 codes [B][H][N][d]
+  const float* sk;     // K block scales [B][H][ceil(N/64)]
+  const uint8_t* v8t;  // E4M3 codes, transposed 64-key tiles [B][H][ceil(N/64)][d][64]
+  const float* sv;     // V column scales [B][H][d]
+  uint16_t* o;
+  float* lse;
+  const int32_t* kv_len;  // device int32[B] or nullptr
+  int B, H, N, d;
+  float scale_log2;  // scale * log2(e)
+  int causal;
+};
+
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_forward_fp8(const Fp8FwdArgs& a, hipStream_t stream);
+hipError_t launch_fp8_quantize_rows(const uint16_t* x, uint8_t* x8, float* scales, const float* signs,
+                                    float post_scale, int B, int H, int N, int d, hipStream_t stream);
+hipError_t launch_fp8_quantize_v(const uint16_t* v, uint8_t* v8t, float* scales, int B, int H, int N, int d,
+                                 hipStream_t stream);
 // passes: bit 0 = dQ pass (dq + row statistics), bit 1 = dK/dV pass
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream, int passes = 3);
 

@@ -156,6 +156,48 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
                     void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
                     const int32_t* kv_len, void* workspace, size_t workspace_bytes, fa_stream_t stream);
 
+/*
+ * FP8 forward with block quantisation and incoherent processing.  The
+ * "FlashAttention" concept wiki page (section FA3 (3), and the cross-cutting insight on
+ * FP8 stability) names the method -- FP8 inputs with FP32 accumulation, block
+ * quantisation, incoherent processing -- and nothing more; the format, block size and
+ * transform below are this library's readings.  Format: OCP E4M3 (1-4-3, bias 7,
+ * subnormals, largest finite 448, 0x7F/0xFF NaN); every conversion rounds to nearest
+ * even after clamping to +-448.  Three steps, each one call:
+ *
+ * fa_fp8_quantize_qk -- block quantisation of Q or K.  x: bf16 [B][H][N][d] (read only);
+ *   x8: E4M3 codes [B][H][N][d] (written); scales: fp32 [B][H][ceil(N/64)] (written),
+ *   one per block of 64 rows of a head.  For each row y = x, or, when signs != NULL
+ *   (device fp32[d] of +-1), y = (x * signs) H_d with H_d the unnormalised d x d
+ *   Sylvester-Hadamard matrix (fast Walsh-Hadamard butterflies in fp32, fixed order:
+ *   stage h = 1, 2, ..., d/2, pairs (i, i+h) -> (a+b, a-b)).  Per block: amax = max |y|,
+ *   code = e4m3(y * (448 / amax)), scale = (amax / 448) * post_scale (all fp32); a block
+ *   of zeros has scale 0 and codes 0.  Incoherent processing rotates Q and K with the
+ *   same signs, which multiplies Q K^T by d: pass post_scale = 1/d for Q (1 for K) so
+ *   that (codes * scales) of Q and K reproduce Q K^T.
+ * fa_fp8_quantize_v -- column quantisation of V.  v: bf16 [B][H][N][d] (read only);
+ *   v8t: E4M3 codes in the layout the forward consumes, [B][H][ceil(N/64)][d][64]
+ *   (written; byte 32*g + p of row c of tile t is the code of V[64 t + key(g, p)][c],
+ *   key(g, p) = 32*(p/16) + 8*((p%16)/4) + 4*g + p%4, g in {0,1}, p in 0..31; keys past N
+ *   hold code 0); scales: fp32 [B][H][d] (written), one per column of a head over all N
+ *   rows, with the formulas above (post_scale 1).  Four kernel launches on `stream`.
+ * fa_forward_fp8 -- O = softmax(scale * Qd Kd^T [+ masks]) Vd for the dequantised
+ *   inputs Qd = q8 * q_scale (per 64-row block), Kd = k8 * k_scale, Vd = v8t * v_scale
+ *   (per column), computed with E4M3 x E4M3 products and fp32 accumulation; P is rounded
+ *   to E4M3 before P V.  o: bf16 [B][H][N][d], lse: fp32 [B][H][N] (natural log, of the
+ *   dequantised scores), both overwritten.  Masks, scale, kv_len and the rules on
+ *   ownership, streams and errors are those of fa_forward_kvlen.
+ *
+ * All pointers are device pointers; x8, q8, k8 and v8t must be 16-byte aligned, scale
+ * arrays 4-byte aligned.  d must be 64 or 128.
+ */
+int fa_fp8_quantize_qk(const void* x, uint8_t* x8, float* scales, const float* signs, float post_scale, int B, int H,
+                       int N, int d, fa_stream_t stream);
+int fa_fp8_quantize_v(const void* v, uint8_t* v8t, float* scales, int B, int H, int N, int d, fa_stream_t stream);
+int fa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                   const uint8_t* v8t, const float* v_scale, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, const int32_t* kv_len, fa_stream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);
 

@@ -161,3 +161,38 @@ def test_gqa_workspace_size(lib):
     need = lib.fa_backward_gqa_workspace_size(1, 2, 1, 128, 64)
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 128, 64, 0.125, 0, None, FAKE)
     assert lib.fa_backward_gqa(*args, need - 1, None) == -5
+
+
+def _fp8(lib, q8=FAKE, sq=FAKE, k8=FAKE, sk=FAKE, v8t=FAKE, sv=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=128,
+         scale=0.125, causal=0):
+    return lib.fa_forward_fp8(q8, sq, k8, sk, v8t, sv, o, lse, B, H, N, d, scale, causal, None, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q8=None), -1), (dict(sq=None), -1), (dict(k8=None), -1), (dict(sk=None), -1), (dict(v8t=None), -1),
+        (dict(sv=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+        (dict(N=0), -2), (dict(B=0), -2), (dict(d=96), -3), (dict(scale=0.0), -4), (dict(scale=float("nan")), -4),
+        (dict(q8=FAKE + 8), -7), (dict(v8t=FAKE + 4), -7), (dict(sk=FAKE + 2), -7), (dict(lse=FAKE + 1), -7),
+    ],
+)
+def test_forward_fp8_rejects(lib, kw, status):
+    assert _fp8(lib, **kw) == status
+
+
+def test_fp8_quantizers_reject(lib):
+    q = lib.fa_fp8_quantize_qk
+    assert q(None, FAKE, FAKE, None, 1.0, 1, 1, 16, 128, None) == -1
+    assert q(FAKE, None, FAKE, None, 1.0, 1, 1, 16, 128, None) == -1
+    assert q(FAKE, FAKE, None, None, 1.0, 1, 1, 16, 128, None) == -1
+    assert q(FAKE, FAKE, FAKE, None, 1.0, 1, 1, 16, 32, None) == -3
+    assert q(FAKE, FAKE, FAKE, None, 0.0, 1, 1, 16, 128, None) == -4
+    assert q(FAKE, FAKE, FAKE, None, float("inf"), 1, 1, 16, 128, None) == -4
+    assert q(FAKE, FAKE + 8, FAKE, None, 1.0, 1, 1, 16, 128, None) == -7
+    assert q(FAKE, FAKE, FAKE, FAKE + 2, 1.0, 1, 1, 16, 128, None) == -7
+    v = lib.fa_fp8_quantize_v
+    assert v(None, FAKE, FAKE, 1, 1, 16, 64, None) == -1
+    assert v(FAKE, FAKE, FAKE, 1, 0, 16, 64, None) == -2
+    assert v(FAKE, FAKE, FAKE, 1, 1, 16, 48, None) == -3
+    assert v(FAKE, FAKE + 4, FAKE, 1, 1, 16, 64, None) == -7
