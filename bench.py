@@ -45,6 +45,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s (bf16, causal & non) + % of MI355X bf16 MFMA peak"
 
@@ -200,10 +201,61 @@ def run_gpu(args):
         e1.record(stream)
         torch.cuda.synchronize()
         roofline["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(e0.elapsed_time(e1) / 10, 4)}
+    if args.fp8:
+        detail.update(run_fp8(fa, wl, torch, dev, stream, t, w, args.fp8_iters))
     sweep = []
     if args.sweep:
         sweep = run_sweep(fa, wl, torch, dev, stream)
     return value, wall, detail, roofline, (B, H, N, d), inp, sweep
+
+
+def run_fp8(fa, wl, torch, dev, stream, t, w, iters):
+    """FP8 forward (block quantisation + incoherent processing) on the bench inputs: the
+    three quantiser calls once per iteration, then fa_forward_fp8 without and with the
+    causal mask, each between its own HIP events; TFLOP/s against the fp8 dense peak."""
+    B, H, N, d = w.shape
+    nb = -(-N // 64)
+    signs = torch.from_numpy(wl.fp8_signs(d, w.seed)).to(dev)
+    q8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=dev)
+    k8 = torch.empty_like(q8)
+    v8t = torch.empty((B, H, nb, d, 64), dtype=torch.uint8, device=dev)
+    sq = torch.empty((B, H, nb), dtype=torch.float32, device=dev)
+    sk = torch.empty_like(sq)
+    sv = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def quant():
+        fa.fa_fp8_quantize_qk(t["q"], q8, sq, signs, 1.0 / d, stream=stream)
+        fa.fa_fp8_quantize_qk(t["k"], k8, sk, signs, 1.0, stream=stream)
+        fa.fa_fp8_quantize_v(t["v"], v8t, sv, stream=stream)
+
+    calls = {"quant": quant}
+    for causal in (False, True):
+        calls[causal] = (lambda c: lambda: fa.fa_forward_fp8(q8, sq, k8, sk, v8t, sv, o, lse, w.scale, c,
+                                                              stream=stream))(causal)
+    for fn in calls.values():
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    ev = {key: [] for key in calls}
+    for _ in range(iters):
+        for key, fn in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev[key].append((e0, e1))
+    torch.cuda.synchronize()
+    ms = {key: sum(a.elapsed_time(b) for a, b in v) / len(v) for key, v in ev.items()}
+    out = {}
+    for causal in (False, True):
+        f = fwd_flops(B, H, N, d, causal)
+        tf = f / (ms[causal] * 1e-3) / 1e12
+        out[f"fwd_fp8_{'causal' if causal else 'full'}"] = {
+            "ms": round(ms[causal], 4), "tflops": round(tf, 1), "pct_peak_fp8": round(100.0 * tf / PEAK_FP8_TFLOPS, 2),
+            "pct_peak_bf16": round(100.0 * tf / PEAK_BF16_TFLOPS, 2), "quantize_ms": round(ms["quant"], 4)}
+    return out
 
 
 def run_sweep(fa, wl, torch, dev, stream, iters=10):
@@ -252,6 +304,10 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
             res[direction] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                               "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                               "alg_gbs": round(_alg_bytes(B, H, N, d, direction, w.kv_heads) / (ms * 1e-3) / 1e9, 1)}
+        if name.startswith("sweep_n"):
+            # the FP8 forward on the same inputs (block quantisation + incoherent processing)
+            res["fwd_fp8"] = {k: v for k, v in run_fp8(fa, wl, torch, dev, stream, t, w, iters)[
+                f"fwd_fp8_{'causal' if w.causal else 'full'}"].items()}
         print(json.dumps({"sweep": res}), file=sys.stderr, flush=True)
         out.append(res)
         del t, o, lse
@@ -360,6 +416,9 @@ def main(argv=None):
     ap.add_argument("--n", type=int, default=8192, help="sequence length of the bench workload (default 8192)")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="also time every workload of the sweep (stderr)")
+    ap.add_argument("--no-fp8", dest="fp8", action="store_false",
+                    help="skip the FP8 forward (timed after the bf16 step, reported under detail)")
+    ap.add_argument("--fp8-iters", type=int, default=20, help="timed iterations of the FP8 forward (default 20)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run 10 plain device copies of {COPY_CAL_MIB} MiB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
