@@ -292,13 +292,18 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
             for _ in range(3):
                 call()
             torch.cuda.synchronize()
+            # at least `iters` calls and about 30 ms of timed work per entry
+            t0 = time.perf_counter()
+            call()
+            torch.cuda.synchronize()
+            n_it = max(iters, int(0.03 / max(time.perf_counter() - t0, 1e-6)))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for _ in range(iters):
+            for _ in range(n_it):
                 call()
             e1.record(stream)
             torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / iters
+            ms = e0.elapsed_time(e1) / n_it
             f = w.fwd_flops() * (1.0 if direction == "fwd" else 2.5)
             tf = f / (ms * 1e-3) / 1e12
             res[direction] = {"ms": round(ms, 4), "tflops": round(tf, 1),

@@ -138,23 +138,33 @@ __global__ __launch_bounds__(64) void fp8_quant_rows_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------------
-// V column quantisation, three launches:
-//  1. column amax of one head, 8 columns (one 16-byte chunk) per workgroup -> amax
-//     (written into the scale output);
+// V column quantisation, four launches:
+//  0. zero the scale output;
+//  1. column amax, 256 rows of one head per workgroup, merged with atomic max into the
+//     scale output;
 //  2. quantise and transpose one 64-key tile per workgroup: V8T[bh][tile][d][64] with
 //     byte 32*h + p of row d = code of V[tile*64 + pv_key(h, p)][d] (zero past N);
 //  3. amax -> scale = amax / 448 in place.
+// (The zeroing is a kernel, not a memset, so the sequence may be captured in a graph.)
 // ---------------------------------------------------------------------------------
+// Column amax over 256 rows of one head per workgroup: 16-byte chunks, D/8 lanes per row
+// (each row read as one contiguous segment), a tree over the rows in LDS, then one
+// atomic max per column into amax (zeroed before; non-negative fp32 values order like
+// their bit patterns, so the unsigned max is the float max and the result does not
+// depend on the order of the workgroups).
+constexpr int kColmaxRows = 256;
 template <int D>
 __global__ __launch_bounds__(256) void fp8_v_colmax_kernel(const uint16_t* __restrict__ v, float* __restrict__ amax,
-                                                            int N) {
-  constexpr int NCH = D / 8;
-  const int ch = (int)(blockIdx.x % NCH);
-  const size_t bh = blockIdx.x / NCH;
-  const int t = threadIdx.x;
+                                                            int N, int nchunks) {
+  constexpr int NCH = D / 8;            // lanes per row
+  constexpr int RPP = 256 / NCH;        // rows per pass
+  const int chunk = (int)(blockIdx.x % (unsigned)nchunks);
+  const size_t bh = blockIdx.x / (unsigned)nchunks;
+  const int t = threadIdx.x, ch = t % NCH, r0 = t / NCH;
   float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const uint16_t* base = v + bh * N * D + 8 * ch;
-  for (int r = t; r < N; r += 256) {
+  const int row_end = min(N, (chunk + 1) * kColmaxRows);
+  for (int r = chunk * kColmaxRows + r0; r < row_end; r += RPP) {
     const u32x4 w = *(const u32x4*)(base + (size_t)r * D);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -162,14 +172,20 @@ __global__ __launch_bounds__(256) void fp8_v_colmax_kernel(const uint16_t* __res
       m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(bf16_hi(w[i])));
     }
   }
-  __shared__ float red[4][8];
+  __shared__ float red[RPP][D + 4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m[i] = wave_max(m[i]);
-  if ((t & 63) == 0)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) red[t >> 6][i] = m[i];
+  for (int i = 0; i < 8; ++i) red[r0][8 * ch + i] = m[i];
   __syncthreads();
-  if (t < 8) amax[bh * D + 8 * ch + t] = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+  for (int c = t; c < D; c += 256) {
+    float x = 0.f;
+    for (int r = 0; r < RPP; ++r) x = fmaxf(x, red[r][c]);
+    atomicMax((unsigned int*)(amax + bh * D + c), __float_as_uint(x));
+  }
+}
+
+__global__ __launch_bounds__(256) void fp8_zero_kernel(float* s, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) s[i] = 0.f;
 }
 
 template <int D>
@@ -500,16 +516,20 @@ hipError_t launch_fp8_quantize_v(const uint16_t* v, uint8_t* v8t, float* scales,
                                  hipStream_t stream) {
   const int nt = (N + kTileKeys - 1) / kTileKeys;
   const unsigned bh = (unsigned)(B * H);
+  const int nchunks = (N + kColmaxRows - 1) / kColmaxRows;
+  const size_t n = (size_t)bh * d;
+  hipLaunchKernelGGL(fp8_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, scales, n);
   if (d == 128) {
-    hipLaunchKernelGGL(fp8_v_colmax_kernel<128>, dim3(bh * 16), dim3(256), 0, stream, v, scales, N);
+    hipLaunchKernelGGL(fp8_v_colmax_kernel<128>, dim3(bh * (unsigned)nchunks), dim3(256), 0, stream, v, scales, N,
+                       nchunks);
     hipLaunchKernelGGL(fp8_v_quant_t_kernel<128>, dim3(bh * (unsigned)nt), dim3(256), 0, stream, v, scales, v8t, N,
                        nt);
   } else {
-    hipLaunchKernelGGL(fp8_v_colmax_kernel<64>, dim3(bh * 8), dim3(256), 0, stream, v, scales, N);
+    hipLaunchKernelGGL(fp8_v_colmax_kernel<64>, dim3(bh * (unsigned)nchunks), dim3(256), 0, stream, v, scales, N,
+                       nchunks);
     hipLaunchKernelGGL(fp8_v_quant_t_kernel<64>, dim3(bh * (unsigned)nt), dim3(256), 0, stream, v, scales, v8t, N,
                        nt);
   }
-  const size_t n = (size_t)bh * d;
   hipLaunchKernelGGL(fp8_amax_to_scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, scales, n);
   return hipGetLastError();
 }
