@@ -311,7 +311,7 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
             res[direction] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                               "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                               "alg_gbs": round(_alg_bytes(B, H, N, d, direction, w.kv_heads) / (ms * 1e-3) / 1e9, 1)}
-        if name.startswith("sweep_n"):
+        if name.startswith("sweep_n") or name == "long_64k":
             # the FP8 forward on the same inputs (block quantisation + incoherent processing)
             res["fwd_fp8"] = {k: v for k, v in run_fp8(fa, wl, torch, dev, stream, t, w, iters)[
                 f"fwd_fp8_{'causal' if w.causal else 'full'}"].items()}
