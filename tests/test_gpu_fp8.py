@@ -236,3 +236,39 @@ def test_forward_fp8_long_context_sampled_rows(gpu):
     worst, rel, lerr = _check_forward(of, lg, qd, kd, vd, w.scale, True, None, rows=rows)
     print(f"long context: max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  LSE {lerr:.2e}", flush=True)
     assert worst <= 1.0 and rel <= 5e-2 and lerr <= 1e-3
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 65])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_fp8_edge_sizes(gpu, N, d, causal):
+    """Degenerate and ragged lengths (one key, less than a tile, exactly one tile, one key
+    into a second tile), both head dims, both masks."""
+    w = wl.get_workload("fp8_outlier")
+    inp, t, shp, signs = _setup(gpu, w, (1, 2, N, d))
+    g = _quantize_gpu(gpu, t, shp, signs)
+    (q8, sq), (k8, sk), (v8, sv) = _quantize_oracle(inp, signs, d)
+    assert np.array_equal(_u8(g["q"][0]), q8) and np.array_equal(_u8(g["k"][0]), k8)
+    assert np.array_equal(_u8(fa.fp8_v8t_to_rows(g["v"][0], N)), v8)
+    of, lg = _run_forward(gpu, g, shp, w.scale, causal)
+    qd, kd, vd = O.dequantize_blocks(q8, sq), O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
+    worst, rel, lerr = _check_forward(of, lg, qd, kd, vd, w.scale, causal, None)
+    assert worst <= 1.0 and lerr <= 1e-3
+    if N == 1:  # one key: O is that key's value row exactly up to bf16 rounding of O
+        assert np.allclose(of[0, :, 0], vd[0, :, 0], rtol=2.0 ** -8, atol=1e-6)
+
+
+def test_forward_fp8_empty_key_range(gpu):
+    """A batch whose key-padding length is 0: every row of it has no admissible key, so O
+    is exactly 0 and LSE is -inf (the other batch is checked against the oracle)."""
+    w = wl.get_workload("bert_large")
+    inp, t, shp, signs = _setup(gpu, w, (2, 2, 130, 64))
+    B, H, N, d = shp
+    kv = np.array([0, 77], dtype=np.int32)
+    g = _quantize_gpu(gpu, t, shp, signs)
+    (q8, sq), (k8, sk), (v8, sv) = _quantize_oracle(inp, signs, d)
+    of, lg = _run_forward(gpu, g, shp, w.scale, False, torch.from_numpy(kv).to(gpu))
+    assert not of[0].any() and np.all(lg[0] == -np.inf)
+    qd, kd, vd = O.dequantize_blocks(q8, sq), O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
+    worst, rel, lerr = _check_forward(of[1:], lg[1:], qd[1:], kd[1:], vd[1:], w.scale, False, kv[1:])
+    assert worst <= 1.0 and lerr <= 1e-3
