@@ -238,12 +238,14 @@ __global__ __launch_bounds__(256) void fp8_amax_to_scale_kernel(float* s, size_t
 
 // ---------------------------------------------------------------------------------
 // Forward.  One workgroup = 4 waves (one per SIMD) = 128 query rows, 32 per wave, and
-// two workgroups per CU: the two waves that share a SIMD belong to different
-// workgroups, so no barrier holds them in step and one's softmax runs beside the
-// other's products (measured 5-10% faster than one 8-wave workgroup of 256 rows with a
-// barrier per tile, and faster than an explicit phase-offset ping-pong of its two wave
-// groups).  K and V^T tiles of 64 keys (fp8) sit in two-slot LDS rings, filled by direct
-// buffer -> LDS copies that overlap the products of earlier tiles.
+// three workgroups per CU (163-166 registers per wave): the three waves that share a
+// SIMD belong to different workgroups, so no barrier holds them in step and one's
+// softmax runs beside another's products.  Measured (B=2, H=16, N=8192, d=128, one box):
+// this straight tile loop at three waves per SIMD 0.60 ms; one 8-wave workgroup of 256
+// rows per CU 0.70; two 4-wave workgroups per CU with the next tile's score products
+// issued under the softmax 0.65; an explicit phase-offset ping-pong of two wave groups
+// 0.79.  K and V^T tiles of 64 keys (fp8) are double-buffered in LDS, filled by direct
+// buffer -> LDS copies that overlap the previous tile's products.
 //
 // LDS tile layouts (16-byte units, XOR-swizzled so that the 16 lanes of an operand
 // read hit 16 different bank groups):
@@ -257,18 +259,16 @@ __device__ __forceinline__ constexpr uint32_t k_unit(uint32_t r, uint32_t j) {
 __device__ __forceinline__ constexpr uint32_t vt_unit(uint32_t d, uint32_t j) { return d * 4 + (j ^ ((d >> 2) & 3)); }
 
 template <int D, bool CAUSAL, bool KVLEN>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
-  constexpr int U = D / 16;                // 16-byte units per K row
-  constexpr int KT_UNITS = kTileKeys * U;  // K tile
-  constexpr int VT_UNITS = D * 4;          // V^T tile
-  constexpr int NKK = D / 64;              // k-steps of S^T = K Q^T
-  constexpr int NDB = D / 32;              // 32-row blocks of O^T
-  constexpr int COPIES = (KT_UNITS + VT_UNITS) / 64 / kWaves;  // copy instructions per wave per step
+__global__ __launch_bounds__(kThreads, 3) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
+  constexpr int U = D / 16;                 // 16-byte units per K row
+  constexpr int KT_UNITS = kTileKeys * U;   // K tile
+  constexpr int VT_UNITS = D * 4;           // V^T tile
+  constexpr int BUF_BYTES = (KT_UNITS + VT_UNITS) * 16;
+  constexpr int NKK = D / 64;  // k-steps of S^T = K Q^T
+  constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  constexpr int COPIES = (KT_UNITS + VT_UNITS) / 64 / kWaves;  // copy instructions per wave per tile
   static_assert(COPIES * 64 * kWaves == KT_UNITS + VT_UNITS, "tile copy must split over the waves");
-  // LDS: two K slots, then two V^T slots
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * (KT_UNITS + VT_UNITS) * 16];
-  auto kslot = [&](int i) { return smem + i * (KT_UNITS * 16); };
-  auto vslot = [&](int i) { return smem + 2 * (KT_UNITS * 16) + i * (VT_UNITS * 16); };
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * BUF_BYTES];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
@@ -321,31 +321,28 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
 
   const buf_rsrc kg = make_rsrc(p.k8 + head, (uint32_t)N * D);
   const buf_rsrc vg = make_rsrc(p.v8t + (size_t)bh * ntk * D * kTileKeys, (uint32_t)ntk * D * kTileKeys);
-  // one copy step: K tile kj into slot kdst and V^T tile vj into slot vdst (a part is
-  // skipped when its tile does not exist).  Instruction ii of wave w fills units
-  // [64*g, 64*g + 64), g = ii*8 + w, of the K units followed by the V^T units; lane l
-  // fills unit 64*g + l with the 16 bytes the swizzle puts there.
-  auto copy_kv = [&](int kj, unsigned char* kdst, int vj, unsigned char* vdst) {
+  // tile copy: instruction ii of wave w fills units [64*g, 64*g + 64), g = ii*kWaves + w, of
+  // the buffer (K tile units first, then V^T units); lane l fills unit 64*g + l with the
+  // 16 bytes the swizzle puts there
+  auto copy_tile = [&](int j, unsigned char* buf) {
 #pragma unroll
     for (int ii = 0; ii < COPIES; ++ii) {
       const int g = ii * kWaves + w;
       const int u = 64 * g + l;
+      unsigned char* dst = buf + (size_t)__builtin_amdgcn_readfirstlane(64 * g) * 16;
       if (64 * g < KT_UNITS) {  // wave-uniform
-        if (kj < ntiles) {
-          const int r = u / U, jj = (u % U) ^ ((r / (16 / U)) % U);
-          const int row = min(kj * kTileKeys + r, N - 1);
-          buf2lds16(kg, (uint32_t)(row * D + 16 * jj), 0u, kdst + (size_t)__builtin_amdgcn_readfirstlane(64 * g) * 16);
-        }
-      } else if (vj < ntiles) {
+        const int r = u / U, jj = (u % U) ^ ((r / (16 / U)) % U);
+        const int row = min(j * kTileKeys + r, N - 1);
+        buf2lds16(kg, (uint32_t)(row * D + 16 * jj), 0u, dst);
+      } else {
         const int v = u - KT_UNITS;
         const int d = v >> 2, jj = (v & 3) ^ ((d >> 2) & 3);
-        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)vj * (D * kTileKeys));
-        buf2lds16(vg, (uint32_t)(d * 64 + 16 * jj), soff,
-                  vdst + (size_t)__builtin_amdgcn_readfirstlane(64 * g - KT_UNITS) * 16);
+        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * (D * kTileKeys));
+        buf2lds16(vg, (uint32_t)(d * 64 + 16 * jj), soff, dst);
       }
     }
   };
-  // per-lane fragment byte offsets inside a slot (the swizzle term depends only on the row)
+  // per-lane fragment byte offsets (the swizzle term depends only on the lane's row)
   uint32_t kfr[2][NKK][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -357,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) vfr[db][s] = vt_unit(32 * db + c, 2 * h + s) * 16;
+    for (int s = 0; s < 2; ++s) vfr[db][s] = (KT_UNITS + vt_unit(32 * db + c, 2 * h + s)) * 16;
 
   f32x16 o[NDB];
 #pragma unroll
@@ -366,42 +363,25 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
   float l_run = 0.f;        // this lane's half of the row sum of P (unrounded, biased by 2^kBias)
   const float sl_q = p.scale_log2 * sq;
 
-  // Pipeline: iteration j runs the softmax and P V of tile j and the scores of tile j+1
-  // (their K fragments are read at the top of the iteration, so the reads complete under
-  // the softmax), and copies K_{j+2}, V_{j+1}.
-  // K runs one tile ahead of V: slot kslot(i & 1) holds K_i, vslot(i & 1) holds V_i.
-  // K_{j+2} overwrites K_j (last read by the scores of tile j, one barrier earlier) and
-  // V_{j+1} overwrites V_{j-1} (last read by P V of tile j-1, one barrier earlier).
-  f32x16 sn[2];  // scores of the next tile
-  auto scores = [&](const unsigned char* kt, i32x8 (&ka)[2][NKK]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        ka[kb][kk] = join8(lds_read128(kt, kfr[kb][kk][0]), lds_read128(kt, kfr[kb][kk][1]));
-  };
-  copy_kv(0, kslot(0), 0, vslot(0));
-  copy_kv(1, kslot(1), ntiles, nullptr);
+  copy_tile(0, smem);
   wait_vmem();
   __syncthreads();
-  {
-    i32x8 ka[2][NKK];
-    scores(kslot(0), ka);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) sn[kb] = mfma_fp8(ka[kb][kk], qf[kk], kk == 0 ? f32x16{} : sn[kb]);
-  }
-  lds_barrier();  // every wave has read K_0 before K_2 is copied over it
   for (int j = 0; j < ntiles; ++j) {
-    f32x16 s[2] = {sn[0], sn[1]};
-    copy_kv(j + 2, kslot(j & 1), j + 1, vslot((j + 1) & 1));
+    unsigned char* cur = smem + (j & 1) * BUF_BYTES;
+    if (j + 1 < ntiles) copy_tile(j + 1, smem + ((j + 1) & 1) * BUF_BYTES);
     const int kt0 = j * kTileKeys;
     if (kt0 < wave_kend) {
-      // K fragments of tile j+1; its scores are consumed only if tile j+1 exists and the
-      // wave attends it (otherwise the slot's contents are irrelevant)
-      i32x8 ka[2][NKK];
-      scores(kslot((j + 1) & 1), ka);
+      // S^T = K_j Q^T, two 32-key blocks
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const i32x8 a = join8(lds_read128(cur, kfr[kb][kk][0]), lds_read128(cur, kfr[kb][kk][1]));
+          s[kb] = mfma_fp8(a, qf[kk], s[kb]);
+        }
+      }
       // online softmax; the block scales of Q and K fold into the one multiplier (where
       // a scale is 0 the scores are exactly 0, and FLT_MIN keeps -inf masks at -inf)
       const float sl = fmaxf(sl_q * sk[j], FLT_MIN);
@@ -445,16 +425,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
         const int kb = i >> 2, r0 = 4 * (i & 3);
         pk[i] = (int)pack_fp8x4(s[kb][r0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3]);
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) sn[kb] = mfma_fp8(ka[kb][kk], qf[kk], kk == 0 ? f32x16{} : sn[kb]);
       l_run += tree_sum<2>(s);
       // O^T += V_j^T P^T
-      const unsigned char* vt = vslot(j & 1);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const i32x8 a = join8(lds_read128(vt, vfr[db][0]), lds_read128(vt, vfr[db][1]));
+        const i32x8 a = join8(lds_read128(cur, vfr[db][0]), lds_read128(cur, vfr[db][1]));
         o[db] = mfma_fp8(a, pk, o[db]);
       }
     }
