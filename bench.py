@@ -17,7 +17,8 @@ not algorithmic work); all halved when causal.
 Printed JSON line (rank 0 only):
   metric, value (TFLOP/s), unit, n_gpus, steps, warmup, ms_per_step, higher_is_better,
   scaling, vs_baseline, dtype, data, config, detail (per call: TFLOP/s, % of the bf16
-  dense peak), roofline (dominant launch, HIP events on the launch stream) and
+  dense peak; "ms" is the mean over the timed steps, with median, min and p90 beside
+  it), roofline (dominant launch, HIP events on the launch stream) and
   cpu_baseline (the fp64 oracle on a bounded sample, host cores of this machine).
 
 Options: --sweep prints one extra line per workload of the sweep to stderr.
@@ -99,6 +100,15 @@ def _alg_bytes(B, H, N, d, direction, hkv=None):
     return 8.0 * rows * d + 8.0 * kv_rows * d + 12.0 * rows
 
 
+def _quantile(xs, q):
+    """Linear-interpolated quantile of a list of timings."""
+    ys = sorted(xs)
+    pos = q * (len(ys) - 1)
+    lo = int(math.floor(pos))
+    hi = min(lo + 1, len(ys) - 1)
+    return ys[lo] + (ys[hi] - ys[lo]) * (pos - lo)
+
+
 def run_gpu(args):
     import torch
     import exact_io_aware_19_amd as fa
@@ -150,6 +160,7 @@ def run_gpu(args):
     wall = time.perf_counter() - t0
 
     kms = {c: sum(a.elapsed_time(b) for a, b in ev[c]) / len(ev[c]) for c in kern_calls}
+    per_step = {c: [a.elapsed_time(b) for a, b in ev[c]] for c in kern_calls}
     step_flops = 0.0
     detail = {}
     for direction in ("fwd", "bwd"):
@@ -157,9 +168,16 @@ def run_gpu(args):
             f = fwd_flops(B, H, N, d, causal) * (1.0 if direction == "fwd" else 2.5)
             step_flops += f
             ms = kms[("fwd", causal)] if direction == "fwd" else kms[("dq", causal)] + kms[("dkdv", causal)]
+            if direction == "fwd":
+                samples = per_step[("fwd", causal)]
+            else:
+                samples = [x + y for x, y in zip(per_step[("dq", causal)], per_step[("dkdv", causal)])]
             tf = f / (ms * 1e-3) / 1e12
             entry = {
                 "ms": round(ms, 4),
+                "ms_median": round(_quantile(samples, 0.5), 4),
+                "ms_min": round(min(samples), 4),
+                "ms_p90": round(_quantile(samples, 0.9), 4),
                 "tflops": round(tf, 1),
                 "pct_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
                 "alg_gbs": round(_alg_bytes(B, H, N, d, direction) / (ms * 1e-3) / 1e9, 1),
@@ -438,7 +456,7 @@ def summarize_pmc(fetch_csv, write_csv, out_md):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30, help="timed steps (default 30: about 200 ms of timed work)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--n", type=int, default=8192, help="sequence length of the bench workload (default 8192)")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle CPU-baseline sample (0 = skip)")
