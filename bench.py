@@ -428,7 +428,7 @@ def summarize_pmc(fetch_csv, write_csv, out_md):
     lines = [
         "# HBM traffic per launch, attention fwd/bwd, B=2 H=16 N=8192 d=128",
         "",
-        "Commands (each on the GPU box, from the repository root, one counter per run):",
+        "Commands (each on one MI355X, from the repository root, one counter per run):",
         "",
         "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration",
         "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration",
@@ -472,7 +472,7 @@ def main(argv=None):
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
     value, wall, detail, roofline, shape, inp, _ = run_gpu(args)
