@@ -272,3 +272,53 @@ def test_forward_fp8_empty_key_range(gpu):
     qd, kd, vd = O.dequantize_blocks(q8, sq), O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
     worst, rel, lerr = _check_forward(of[1:], lg[1:], qd[1:], kd[1:], vd[1:], w.scale, False, kv[1:])
     assert worst <= 1.0 and lerr <= 1e-3
+
+
+def _bf16_tensor(gpu, x):
+    bits = wl.f32_to_bf16_bits(x)
+    return bits, torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(gpu)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_quantizers_bit_exact_extreme_values(gpu, d, rotate):
+    """Adversarial inputs for the quantisers: values spread over 10^-20 .. 10^20 inside one
+    block (many subnormal and zero codes), an all-zero block, negative zeros, a single huge
+    outlier, and values that land exactly on E4M3 rounding ties after scaling.  Magnitudes
+    stay where the rotation's fp32 sums cannot overflow."""
+    rng = np.random.default_rng(99)
+    B, H, N = 1, 2, 200
+    x = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    x *= np.exp(rng.uniform(-46, 46, size=x.shape)).astype(np.float32)  # ~1e-20 .. 1e20
+    x[0, 0, 64:128] = 0.0                                              # a block of zeros
+    x[0, 0, 64:70, :7] = -0.0
+    x[0, 1, 130, 5] = 3.0e30                                           # one huge outlier
+    # ties: block amax 448 makes inv = 1, so midpoints between E4M3 neighbours stay ties
+    vals = O.e4m3_decode(np.arange(1, 0x7E, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    tie_rows = np.resize(mids, (64, d)).astype(np.float32)
+    tie_rows[0, 0] = 448.0
+    x[0, 1, 0:64] = tie_rows
+    x = wl.bf16_bits_to_f64(wl.f32_to_bf16_bits(x)).astype(np.float32)  # what the GPU receives
+    bits, xt = _bf16_tensor(gpu, x)
+    signs = wl.fp8_signs(d, 5) if rotate else None
+    nb = -(-N // 64)
+    x8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=gpu)
+    sc = torch.empty((B, H, nb), dtype=torch.float32, device=gpu)
+    fa.fa_fp8_quantize_qk(xt, x8, sc, None if signs is None else torch.from_numpy(signs).to(gpu),
+                          1.0 / d if rotate else 1.0)
+    v8t = torch.empty((B, H, nb, d, 64), dtype=torch.uint8, device=gpu)
+    sv = torch.empty((B, H, d), dtype=torch.float32, device=gpu)
+    fa.fa_fp8_quantize_v(xt, v8t, sv)
+    torch.cuda.synchronize()
+    xr = wl.bf16_bits_to_f64(bits)
+    c_ref, s_ref = O.quantize_blocks(xr, signs, post_scale=1.0 / d if rotate else 1.0)
+    v_ref, sv_ref = O.quantize_columns(xr)
+    assert np.array_equal(_u8(x8), c_ref)
+    assert np.array_equal(sc.cpu().numpy(), s_ref)
+    assert np.array_equal(_u8(fa.fp8_v8t_to_rows(v8t, N)), v_ref)
+    assert np.array_equal(sv.cpu().numpy(), sv_ref)
+    if not rotate:  # the zero block: scale 0, every code a zero (+0 or, for -0.0, 0x80)
+        assert sc.cpu().numpy()[0, 0, 1] == 0.0
+        assert np.all(O.e4m3_decode(_u8(x8)[0, 0, 64:128]) == 0.0)
+        assert np.all(_u8(x8)[0, 0, 64:70, :7] == 0x80)
