@@ -19,6 +19,7 @@
 // round to nearest even (v_cvt_pk_fp8_f32, checked on gfx950 against the format's
 // definition), inputs clamped to +-448 first.
 #include <float.h>
+#include <type_traits>
 
 #include "common.hpp"
 #include "fa_kernels.hpp"
@@ -238,13 +239,13 @@ __global__ __launch_bounds__(256) void fp8_amax_to_scale_kernel(float* s, size_t
 
 // ---------------------------------------------------------------------------------
 // Forward.  One workgroup = 4 waves (one per SIMD) = 128 query rows, 32 per wave, and
-// three workgroups per CU (163-166 registers per wave): the three waves that share a
+// three workgroups per CU (166-168 registers per wave): the three waves that share a
 // SIMD belong to different workgroups, so no barrier holds them in step and one's
 // softmax runs beside another's products.  Measured (B=2, H=16, N=8192, d=128, one box):
-// this straight tile loop at three waves per SIMD 0.60 ms; one 8-wave workgroup of 256
-// rows per CU 0.70; two 4-wave workgroups per CU with the next tile's score products
-// issued under the softmax 0.65; an explicit phase-offset ping-pong of two wave groups
-// 0.79.  K and V^T tiles of 64 keys (fp8) are double-buffered in LDS, filled by direct
+// this straight tile loop at three waves per SIMD 0.60 ms, 3-4% less with the loop run
+// in pairs of tiles (below); one 8-wave workgroup of 256 rows per CU 0.70; two 4-wave
+// workgroups per CU with the next tile's score products issued under the softmax 0.65;
+// an explicit phase-offset ping-pong of two wave groups 0.79.  K and V^T tiles of 64 keys (fp8) are double-buffered in LDS, filled by direct
 // buffer -> LDS copies that overlap the previous tile's products.
 //
 // LDS tile layouts (16-byte units, XOR-swizzled so that the 16 lanes of an operand
@@ -366,9 +367,12 @@ __global__ __launch_bounds__(kThreads, 3) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
   copy_tile(0, smem);
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    unsigned char* cur = smem + (j & 1) * BUF_BYTES;
-    if (j + 1 < ntiles) copy_tile(j + 1, smem + ((j + 1) & 1) * BUF_BYTES);
+  // tiles run in pairs so that the LDS buffer of each tile is a compile-time constant:
+  // fragment addresses are then per-lane bases plus immediate offsets
+  auto tile_step = [&](int j, auto par_c) {
+    constexpr int PAR = decltype(par_c)::value;
+    unsigned char* cur = smem + PAR * BUF_BYTES;
+    if (j + 1 < ntiles) copy_tile(j + 1, smem + (1 - PAR) * BUF_BYTES);
     const int kt0 = j * kTileKeys;
     if (kt0 < wave_kend) {
       // S^T = K_j Q^T, two 32-key blocks
@@ -435,6 +439,10 @@ __global__ __launch_bounds__(kThreads, 3) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
     }
     wait_vmem();
     __syncthreads();
+    };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile_step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntiles) tile_step(j + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: normalise once, apply V's column scales, store O and LSE
