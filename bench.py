@@ -18,8 +18,11 @@ Printed JSON line (rank 0 only):
   metric, value (TFLOP/s), unit, n_gpus, steps, warmup, ms_per_step, higher_is_better,
   scaling, vs_baseline, dtype, data, config, detail (per call: TFLOP/s, % of the bf16
   dense peak; "ms" is the mean over the timed steps, with median, min and p90 beside
-  it), roofline (dominant launch, HIP events on the launch stream) and
-  cpu_baseline (the fp64 oracle on a bounded sample, host cores of this machine).
+  it; "machine": the bf16 MFMA, v_exp_f32, LDS-read and fp32-atomic rates the chip
+  sustains, from the microbenchmark library), roofline (dominant launch, HIP events on
+  the launch stream; "frac_of_sustained_mfma" is its rate against the measured MFMA
+  rate) and cpu_baseline (the fp64 oracle on a bounded sample, host cores of this
+  machine).
 
 Options: --sweep prints one extra line per workload of the sweep to stderr.
 Profiling helpers (rocprofv3 runs whose summaries are committed under profiles/):
@@ -64,14 +67,14 @@ COPY_CAL_MIB = 256  # plain device copy that calibrates FETCH_SIZE / WRITE_SIZE
 
 
 def kernel_source_hash():
-    """Hash of the HIP/C++ sources of the library: a traffic figure taken on other
-    sources is stale."""
-    src = os.path.join(ROOT, "exact_io_aware_19_amd", "csrc")
+    """Hash of the HIP/C++ sources of the attention library: a traffic figure taken on
+    other sources is stale."""
+    from exact_io_aware_19_amd.build import CSRC, KERNEL_SOURCES
+
     h = hashlib.sha256()
-    for name in sorted(os.listdir(src)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(src, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(KERNEL_SOURCES):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -278,6 +281,62 @@ def run_fp8(fa, wl, torch, dev, stream, t, w, iters):
     return out
 
 
+def run_machine(torch, dev, stream, reps=3):
+    """Machine microbenchmarks (libfa355_micro.so, include/fa_micro.h), each launched
+    `reps` times between HIP events on the bench stream; the median is reported.  They
+    give what the chip sustains at its running clock: the bf16 MFMA rate, the v_exp_f32
+    rate, LDS read bandwidth and fp32 atomic-add throughput."""
+    import ctypes
+
+    from exact_io_aware_19_amd.build import MICRO_LIB_PATH
+
+    if not os.path.exists(MICRO_LIB_PATH):
+        raise RuntimeError(f"{MICRO_LIB_PATH} is missing: build it with `python -m exact_io_aware_19_amd.build`")
+    lib = ctypes.CDLL(MICRO_LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    for name in ("fa_micro_mfma_bf16", "fa_micro_exp", "fa_micro_lds_read"):
+        getattr(lib, name).argtypes = [vp, i, i, vp]
+        getattr(lib, name).restype = i
+    lib.fa_micro_atomic_tiles.argtypes = [vp, i, i, i, vp]
+    lib.fa_micro_atomic_tiles.restype = i
+    lib.fa_micro_grid_blocks.restype = i
+    blocks = lib.fa_micro_grid_blocks()
+    if blocks < 1:
+        raise RuntimeError("fa_micro_grid_blocks failed")
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    ntiles, tiles = 4096, 64
+    buf = torch.zeros(ntiles * 64 * 128, dtype=torch.float32, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    iters = {"mfma": 20000, "exp": 50000, "lds": 20000}
+    # (call, units of work per call, scale to the reported unit)
+    cases = {
+        "mfma_bf16_tflops": (lambda: lib.fa_micro_mfma_bf16(out.data_ptr(), blocks, iters["mfma"], sp),
+                             blocks * 4 * 8 * iters["mfma"] * 32768, 1e-12),
+        "exp2_gops": (lambda: lib.fa_micro_exp(out.data_ptr(), blocks, iters["exp"], sp),
+                      blocks * 256 * 16 * iters["exp"], 1e-9),
+        "lds_read_tbs": (lambda: lib.fa_micro_lds_read(out.data_ptr(), blocks, iters["lds"], sp),
+                         blocks * 4 * 8 * iters["lds"] * 1024, 1e-12),
+        "atomic_f32_gbs": (lambda: lib.fa_micro_atomic_tiles(buf.data_ptr(), ntiles, blocks, tiles, sp),
+                           blocks * tiles * 64 * 128 * 4, 1e-9),
+    }
+    res = {}
+    for key, (call, work, unit) in cases.items():
+        if call() != 0:  # warm-up launch, also checks the arguments
+            raise RuntimeError(f"{key}: launch failed")
+        evs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
+        res[key] = round(work / (ms * 1e-3) * unit, 1)
+    res["mfma_bf16_pct_of_peak"] = round(100.0 * res["mfma_bf16_tflops"] / PEAK_BF16_TFLOPS, 1)
+    return res
+
+
 def _lib_handle():
     from exact_io_aware_19_amd import _lib
 
@@ -464,6 +523,8 @@ def main(argv=None):
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the FP8 forward (timed after the bf16 step, reported under detail)")
     ap.add_argument("--fp8-iters", type=int, default=20, help="timed iterations of the FP8 forward (default 20)")
+    ap.add_argument("--no-machine", dest="machine", action="store_false",
+                    help="skip the machine microbenchmarks (sustained MFMA, exp, LDS, atomic rates)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run 10 plain device copies of {COPY_CAL_MIB} MiB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
@@ -477,6 +538,12 @@ def main(argv=None):
 
     value, wall, detail, roofline, shape, inp, _ = run_gpu(args)
     B, H, N, d = shape
+    if args.machine:
+        import torch
+
+        detail["machine"] = m = run_machine(torch, torch.device("cuda:0"), torch.cuda.current_stream())
+        # the dominant kernel against the MFMA rate the chip sustains, beside the data-sheet peak
+        roofline["frac_of_sustained_mfma"] = round(roofline["achieved"] / m["mfma_bf16_tflops"], 4)
     cpu = None
     if args.cpu_heads > 0:
         import numpy as np

@@ -1,8 +1,9 @@
-"""Build libfa355.so in-tree with hipcc for gfx950.
+"""Build libfa355.so (attention) and libfa355_micro.so (machine microbenchmarks)
+in-tree with hipcc for gfx950.
 
     python -m exact_io_aware_19_amd.build [--verbose]
 
-Each source is compiled separately (parallel), then linked into one shared library
+Each source is compiled separately (parallel), then linked into its shared library
 next to this file.  Kernel resource usage (VGPR/AGPR/LDS/spills) is written to
 ``_build/resource_usage.txt`` for inspection.
 """
@@ -22,6 +23,10 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_api.cpp"]
+# sources of the attention library's kernels (a profile taken on other ones is stale)
+KERNEL_SOURCES = SOURCES + ["common.hpp", "fa_kernels.hpp"]
+MICRO_SOURCES = ["micro.hip"]
+MICRO_LIB_PATH = os.path.join(PKG_DIR, "libfa355_micro.so")
 
 COMMON_FLAGS = [
     "-O3",
@@ -57,22 +62,27 @@ def _compile(src, verbose):
     return obj, r.stderr
 
 
-def build(verbose=False):
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    objs = [o for o, _ in results]
-    usage = "\n".join(err for _, err in results if "resource usage" in err.lower() or "remark" in err)
-    with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
-        f.write(usage)
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path, verbose):
+    tmp = path + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking {LIB_NAME} failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"linking {os.path.basename(path)} failed:\n{r.stderr}")
+    os.replace(tmp, path)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {path}")
+
+
+def build(verbose=False):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + MICRO_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        results = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    usage = "\n".join(err for _, err in results.values() if "resource usage" in err.lower() or "remark" in err)
+    with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
+        f.write(usage)
+    _link([results[s][0] for s in SOURCES], LIB_PATH, verbose)
+    _link([results[s][0] for s in MICRO_SOURCES], MICRO_LIB_PATH, verbose)
     return LIB_PATH
 
 

@@ -1,0 +1,134 @@
+// Microbenchmarks of the gfx950 units the attention kernels are bound by: the bf16 MFMA
+// rate the chip sustains (its clock under load included), the v_exp_f32 rate, LDS read
+// bandwidth and fp32 global atomic throughput.  They measure the machine, not attention:
+// the bench reports them beside the data-sheet peaks.  C ABI in include/fa_micro.h
+// (libfa355_micro.so, a library of its own).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fa_micro.h"
+#include "common.hpp"
+
+namespace fa355 {
+namespace {
+
+constexpr int kMicroThreads = 256;  // 4 waves, one per SIMD
+constexpr int kMicroBlocksPerCU = 2;
+
+// Eight independent chains of v_mfma_f32_32x32x16_bf16 per wave; all SIMDs of the GPU run
+// two such waves.  One product = 2*32*32*16 = 32768 FLOP.
+__global__ __launch_bounds__(kMicroThreads, kMicroBlocksPerCU) void mfma_bf16_loop(float* __restrict__ out, int iters) {
+  const int tid = threadIdx.x;
+  // bf16 2^-10 (0x3A80) in every operand element: accumulators grow by 16 * 2^-20 per
+  // product, far from overflow
+  const u32x4 a = {0x3A803A80u, 0x3A803A80u, 0x3A803A80u, 0x3A803A80u};
+  const u32x4 b = a;
+  f32x16 acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = mfma32(a, b, acc[k]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[k][r];
+  out[(size_t)blockIdx.x * kMicroThreads + tid] = s;
+}
+
+// Sixteen independent chains x <- exp2(-x) per lane (x stays in (0, 1]).
+__global__ __launch_bounds__(kMicroThreads, kMicroBlocksPerCU) void exp_loop(float* __restrict__ out, int iters) {
+  const int tid = threadIdx.x;
+  float x[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = 0.25f + 0.03f * k + 1e-6f * tid;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = __builtin_amdgcn_exp2f(-x[k]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) s += x[k];
+  out[(size_t)blockIdx.x * kMicroThreads + tid] = s;
+}
+
+// 128-bit LDS reads: each wave reads 1 KiB contiguous per instruction (conflict free),
+// eight reads in flight per lane, XOR-accumulated.  The window moves by 16 bytes per
+// iteration so no read can be hoisted out of the loop; the largest byte read is
+// 16*63 + 1024*3 + 16*63 + 4096*7 + 16 = 33776 < 40960.
+constexpr uint32_t kMicroLdsBytes = 40960;
+__global__ __launch_bounds__(kMicroThreads, kMicroBlocksPerCU) void lds_read_loop(float* __restrict__ out, int iters) {
+  __shared__ __attribute__((aligned(16))) unsigned char tile[kMicroLdsBytes];
+  const int tid = threadIdx.x;
+  for (uint32_t i = tid; i < kMicroLdsBytes / 16; i += kMicroThreads) {
+    const u32x4 v = {i, i * 3u, i * 5u, i * 7u};
+    lds_write128(tile, 16u * i, v);
+  }
+  __syncthreads();
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const uint32_t base = 16u * (uint32_t)(tid & 63) + 1024u * (uint32_t)(tid >> 6);
+  for (int i = 0; i < iters; ++i) {
+    const uint32_t off = base + 16u * (uint32_t)(i & 63);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= lds_read128(tile, off + 4096u * (uint32_t)k);
+  }
+  out[(size_t)blockIdx.x * kMicroThreads + tid] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
+// fp32 atomic adds of whole 64x128 tiles (32 KB), the pattern an atomic dQ accumulation
+// would write: workgroup w adds `tiles` tiles at tile positions (w + t) % ntiles of buf.
+__global__ __launch_bounds__(kMicroThreads) void atomic_tiles(float* __restrict__ buf, int ntiles, int tiles) {
+  const int w = blockIdx.x;
+  for (int t = 0; t < tiles; ++t) {
+    float* tile = buf + (size_t)((w + t) % ntiles) * 64 * 128;
+    for (int e = threadIdx.x; e < 64 * 128; e += kMicroThreads) atomicAdd(tile + e, 1.0f);
+  }
+}
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return n;
+}
+
+}  // namespace
+}  // namespace fa355
+
+extern "C" {
+
+int fa_micro_grid_blocks(void) {
+  const int n = fa355::cu_count();
+  return n > 0 ? n * fa355::kMicroBlocksPerCU : -1;
+}
+
+int fa_micro_mfma_bf16(float* out, int blocks, int iters, fa_stream_t stream) {
+  if (!out || blocks < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(fa355::mfma_bf16_loop, dim3(blocks), dim3(fa355::kMicroThreads), 0, (hipStream_t)stream, out,
+                     iters);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int fa_micro_exp(float* out, int blocks, int iters, fa_stream_t stream) {
+  if (!out || blocks < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(fa355::exp_loop, dim3(blocks), dim3(fa355::kMicroThreads), 0, (hipStream_t)stream, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int fa_micro_lds_read(float* out, int blocks, int iters, fa_stream_t stream) {
+  if (!out || blocks < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(fa355::lds_read_loop, dim3(blocks), dim3(fa355::kMicroThreads), 0, (hipStream_t)stream, out,
+                     iters);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int fa_micro_atomic_tiles(float* buf, int ntiles, int blocks, int tiles, fa_stream_t stream) {
+  if (!buf || ntiles < 1 || blocks < 1 || tiles < 1) return -1;
+  hipLaunchKernelGGL(fa355::atomic_tiles, dim3(blocks), dim3(fa355::kMicroThreads), 0, (hipStream_t)stream, buf,
+                     ntiles, tiles);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // extern "C"

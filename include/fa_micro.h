@@ -1,0 +1,56 @@
+/*
+ * fa_micro.h -- C ABI of the machine microbenchmarks (libfa355_micro.so).
+ *
+ * These kernels measure the gfx950 units the attention kernels are bound by, under load
+ * on every compute unit: the bf16 matrix-core (MFMA) rate, the v_exp_f32 rate, LDS read
+ * bandwidth and fp32 global atomic-add throughput.  They compute nothing of attention;
+ * the bench reports them beside the data-sheet peaks so that a kernel's fraction of peak
+ * can also be read against what the chip sustains at its running clock.
+ *
+ * Conventions
+ *  - `out` / `buf` are DEVICE pointers to float32 arrays owned by the caller.
+ *  - `blocks` is the grid size in workgroups of 256 threads; fa_micro_grid_blocks()
+ *    returns the size that puts two workgroups on every compute unit (or -1 if the
+ *    device cannot be queried).
+ *  - Every call only enqueues one kernel on `stream` (0 = the null stream) and returns;
+ *    it never allocates or synchronises.  Time it with events on the same stream.
+ *  - Return value: 0 on success, -1 for a NULL pointer or a count below 1 (nothing is
+ *    enqueued), -6 when the launch fails.
+ */
+#ifndef FA355_FA_MICRO_H
+#define FA355_FA_MICRO_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* fa_stream_t; /* identical to hipStream_t */
+
+/* Workgroups that put two 256-thread workgroups on every compute unit, or -1. */
+int fa_micro_grid_blocks(void);
+
+/* bf16 MFMA rate: every wave runs 8 independent accumulation chains of `iters`
+ * v_mfma_f32_32x32x16_bf16 products (32768 FLOP each), so one call performs
+ * blocks * 4 * 8 * iters * 32768 FLOP.  `out` holds blocks * 256 floats (one sum of
+ * accumulators per thread, written so the work is not removed). */
+int fa_micro_mfma_bf16(float* out, int blocks, int iters, fa_stream_t stream);
+
+/* v_exp_f32 rate: every thread runs 16 independent chains of `iters` exponentials
+ * (blocks * 256 * 16 * iters in total).  `out` holds blocks * 256 floats. */
+int fa_micro_exp(float* out, int blocks, int iters, fa_stream_t stream);
+
+/* LDS read bandwidth: every wave issues 8 * iters 128-bit reads of 1 KiB contiguous
+ * (bank-conflict free) from a 40 KiB tile, blocks * 4 * 8 * iters KiB in total.
+ * `out` holds blocks * 256 floats. */
+int fa_micro_lds_read(float* out, int blocks, int iters, fa_stream_t stream);
+
+/* fp32 global atomic-add throughput on whole 64 x 128 tiles (32 KiB): workgroup w adds
+ * 1.0 to every element of the `tiles` tiles at positions (w + t) % ntiles of `buf`, which
+ * holds ntiles * 8192 floats; blocks * tiles * 8192 atomic adds in total. */
+int fa_micro_atomic_tiles(float* buf, int ntiles, int blocks, int tiles, fa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_FA_MICRO_H */

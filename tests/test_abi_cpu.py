@@ -196,3 +196,32 @@ def test_fp8_quantizers_reject(lib):
     assert v(FAKE, FAKE, FAKE, 1, 0, 16, 64, None) == -2
     assert v(FAKE, FAKE, FAKE, 1, 1, 16, 48, None) == -3
     assert v(FAKE, FAKE + 4, FAKE, 1, 1, 16, 64, None) == -7
+
+
+MICRO_HEADER = os.path.join(ROOT, "include", "fa_micro.h")
+
+
+def test_micro_library_exports_every_declared_symbol():
+    """The machine-microbenchmark library (include/fa_micro.h) loads and exports every
+    declared entry point; its argument checks return -1 before any HIP call."""
+    from exact_io_aware_19_amd.build import MICRO_LIB_PATH
+
+    if not os.path.exists(MICRO_LIB_PATH):
+        pytest.fail(f"{MICRO_LIB_PATH} not built; run python -m exact_io_aware_19_amd.build")
+    with open(MICRO_HEADER) as f:
+        names = sorted(set(re.findall(r"^\s*int\s+(fa_micro_\w+)\s*\(", f.read(), re.M)))
+    assert names == ["fa_micro_atomic_tiles", "fa_micro_exp", "fa_micro_grid_blocks", "fa_micro_lds_read",
+                     "fa_micro_mfma_bf16"]
+    lib = ctypes.CDLL(MICRO_LIB_PATH)
+    for name in names:
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr), name
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    for name in ("fa_micro_mfma_bf16", "fa_micro_exp", "fa_micro_lds_read"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, i, i, vp]
+        assert fn(None, 1, 1, None) == -1
+        assert fn(vp(16), 0, 1, None) == -1
+        assert fn(vp(16), 1, 0, None) == -1
+    lib.fa_micro_atomic_tiles.argtypes = [vp, i, i, i, vp]
+    assert lib.fa_micro_atomic_tiles(None, 1, 1, 1, None) == -1
+    assert lib.fa_micro_atomic_tiles(vp(16), 0, 1, 1, None) == -1
