@@ -1,0 +1,108 @@
+"""GPU checks of the machine microbenchmarks (include/fa_micro.h): each kernel computes
+exactly what its header says, so the rates the bench derives from them count real work.
+Small grids and iteration counts; the expected values are worked out here in Python."""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS = 6  # workgroups of 256 threads
+
+
+@pytest.fixture(scope="module")
+def micro():
+    from exact_io_aware_19_amd.build import MICRO_LIB_PATH
+
+    if not os.path.exists(MICRO_LIB_PATH):
+        pytest.fail(f"{MICRO_LIB_PATH} not built; run python -m exact_io_aware_19_amd.build")
+    lib = ctypes.CDLL(MICRO_LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    for name in ("fa_micro_mfma_bf16", "fa_micro_exp", "fa_micro_lds_read"):
+        getattr(lib, name).argtypes = [vp, i, i, vp]
+        getattr(lib, name).restype = i
+    lib.fa_micro_atomic_tiles.argtypes = [vp, i, i, i, vp]
+    lib.fa_micro_atomic_tiles.restype = i
+    lib.fa_micro_grid_blocks.restype = i
+    return lib
+
+
+def _run(gpu, fn, *args):
+    import torch
+
+    out = torch.full((BLOCKS * 256,), -1.0, dtype=torch.float32, device=gpu)
+    assert fn(out.data_ptr(), BLOCKS, *args, None) == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_grid_blocks(gpu, micro):
+    import torch
+
+    P.say("micro grid blocks")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert micro.fa_micro_grid_blocks() == 2 * cus
+
+
+def test_mfma_loop_sums(gpu, micro):
+    # every operand element is bf16 2^-10: one 32x32x16 product adds 16 * 2^-20 = 2^-16 to
+    # each of a lane's 16 accumulators; 8 chains x 16 accumulators x iters products
+    P.say("micro mfma")
+    iters = 40
+    out = _run(gpu, micro.fa_micro_mfma_bf16, iters)
+    np.testing.assert_array_equal(out, np.float32(8 * 16 * iters * 2.0**-16))
+
+
+def test_exp_loop_values(gpu, micro):
+    # 16 chains x <- 2^(-x) per thread from x0 = 0.25 + 0.03 k + 1e-6 tid; the map is a
+    # contraction (|d/dx| <= ln2 * 2^-0.25 < 0.6), so rounding differences stay small
+    P.say("micro exp")
+    iters = 25
+    out = _run(gpu, micro.fa_micro_exp, iters)
+    tid = np.arange(256, dtype=np.float64)
+    x = 0.25 + 0.03 * np.arange(16)[:, None] + 1e-6 * tid[None, :]
+    for _ in range(iters):
+        x = np.exp2(-x)
+    want = np.tile(x.sum(axis=0), BLOCKS)
+    np.testing.assert_allclose(out, want, rtol=2e-5, atol=0)
+
+
+def test_lds_read_xor(gpu, micro):
+    # tile unit u (16 bytes) holds (u, 3u, 5u, 7u); thread t reads, per iteration i and
+    # k < 8, unit (t % 64) + 64 (t // 64) + (i % 64) + 256 k, XOR-accumulating the words
+    P.say("micro lds")
+    iters = 70
+    out = _run(gpu, micro.fa_micro_lds_read, iters)
+    want = np.zeros(256)
+    for t in range(256):
+        acc = [0, 0, 0, 0]
+        for i in range(iters):
+            for k in range(8):
+                u = (t % 64) + 64 * (t // 64) + (i % 64) + 256 * k
+                acc = [a ^ (m * u) for a, m in zip(acc, (1, 3, 5, 7))]
+        want[t] = float(acc[0] ^ acc[1] ^ acc[2] ^ acc[3])
+    np.testing.assert_array_equal(out, np.tile(want, BLOCKS).astype(np.float32))
+
+
+def test_atomic_tiles_counts(gpu, micro):
+    # workgroup w adds 1.0 to every element of tiles (w + t) % ntiles, t < tiles: each
+    # tile ends with the number of (w, t) pairs that hit it
+    import torch
+
+    P.say("micro atomics")
+    ntiles, tiles, blocks = 5, 3, 7
+    buf = torch.zeros(ntiles * 64 * 128, dtype=torch.float32, device=gpu)
+    for _ in range(2):  # two calls accumulate
+        assert micro.fa_micro_atomic_tiles(buf.data_ptr(), ntiles, blocks, tiles, None) == 0
+    torch.cuda.synchronize()
+    hits = np.zeros(ntiles)
+    for w in range(blocks):
+        for t in range(tiles):
+            hits[(w + t) % ntiles] += 2
+    got = buf.cpu().numpy().reshape(ntiles, 64 * 128)
+    np.testing.assert_array_equal(got, np.repeat(hits[:, None], 64 * 128, axis=1).astype(np.float32))
