@@ -211,6 +211,9 @@ def run_gpu(args):
     }
     if args.fp8:
         detail.update(run_fp8(fa, wl, torch, dev, stream, t, w, args.fp8_iters))
+    sweep = []
+    if args.sweep:
+        sweep = run_sweep(fa, wl, torch, dev, stream)
     # the calibration copies come last: the counter summary takes the last ten copy
     # dispatches of the run
     if args.copy_calibration:
@@ -226,9 +229,6 @@ def run_gpu(args):
         e1.record(stream)
         torch.cuda.synchronize()
         roofline["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(e0.elapsed_time(e1) / 10, 4)}
-    sweep = []
-    if args.sweep:
-        sweep = run_sweep(fa, wl, torch, dev, stream)
     return value, wall, detail, roofline, (B, H, N, d), inp, sweep
 
 
@@ -453,18 +453,24 @@ def cpu_baseline(inp, shape, heads):
     }
 
 
-def summarize_pmc(fetch_csv, write_csv, out_md):
+def summarize_pmc(fetch_csv, write_csv, out_md, by_grid=False):
     """HBM bytes per launch of every kernel of the bench step from two rocprofv3 --pmc
     runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same
     counter reads for the last ten plain copies (bench.py --copy-calibration), whose
-    bytes are known."""
+    bytes are known.  by_grid: one row per kernel and grid size (workgroups), for runs
+    that launch one kernel on several workload shapes (--sweep)."""
 
     def load(path, counter):
         rows = []
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
-                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+                    name = r["Kernel_Name"]
+                    if by_grid and "fa355" in name:
+                        wg = max(1, int(r["Workgroup_Size"]))
+                        bare = name.replace("void ", "", 1).replace("fa355::(anonymous namespace)::", "").split("(")[0]
+                        name = "fa355::(anonymous namespace)::%s grid=%d" % (bare, int(r["Grid_Size"]) // wg)
+                    rows.append((int(r["Dispatch_Id"]), name, float(r["Counter_Value"])))
         return sorted(rows)
 
     out = {}
@@ -484,14 +490,18 @@ def summarize_pmc(fetch_csv, write_csv, out_md):
                 per.setdefault(key, []).append(v)
         out[counter] = {kname: sum(vs) / len(vs) for kname, vs in per.items()}
     m = re.search(r"--copy-calibration (\d+)", " ".join(sys.argv))
+    sweep = " --sweep --no-machine" if by_grid else ""
+    tag = "_sweep" if by_grid else ""
     lines = [
-        "# HBM traffic per launch, attention fwd/bwd, B=2 H=16 N=8192 d=128",
+        "# HBM traffic per launch, attention fwd/bwd, "
+        + ("every workload of the sweep (one row per kernel and grid)" if by_grid else "B=2 H=16 N=8192 d=128"),
         "",
         "Commands (each on one MI355X, from the repository root, one counter per run):",
         "",
-        "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration",
-        "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration",
-        "    python bench.py --summarize-pmc gpurun_out/pmc_fetch/p_counter_collection.csv gpurun_out/pmc_write/p_counter_collection.csv " + os.path.relpath(out_md, ROOT),
+        "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch%s -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration%s" % (tag, sweep),
+        "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write%s -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration%s" % (tag, sweep),
+        "    python bench.py --summarize-pmc%s gpurun_out/pmc_fetch%s/p_counter_collection.csv gpurun_out/pmc_write%s/p_counter_collection.csv %s"
+        % (" --pmc-by-grid" if by_grid else "", tag, tag, os.path.relpath(out_md, ROOT)),
         "",
         "Calibration: the last ten dispatches of the plain %d MiB device copy read and write" % COPY_CAL_MIB,
         "%d bytes each; the counters read %.0f KiB (FETCH_SIZE) and %.0f KiB (WRITE_SIZE)," % (COPY_CAL_MIB << 20, cal["FETCH_SIZE"], cal["WRITE_SIZE"]),
@@ -505,7 +515,8 @@ def summarize_pmc(fetch_csv, write_csv, out_md):
     for kname in sorted(out["FETCH_SIZE"]):
         fb = out["FETCH_SIZE"][kname] * 1024 * kib / cal["FETCH_SIZE"]
         wb = out["WRITE_SIZE"].get(kname, 0.0) * 1024 * kib / cal["WRITE_SIZE"]
-        lines.append("| %s | %.0f | %.0f | %.0f |" % (kname, fb + wb, fb, wb))
+        shown = kname.replace("void ", "", 1).replace("fa355::(anonymous namespace)::", "")
+        lines.append("| %s | %.0f | %.0f | %.0f |" % (shown, fb + wb, fb, wb))
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -527,11 +538,13 @@ def main(argv=None):
                     help="skip the machine microbenchmarks (sustained MFMA, exp, LDS, atomic rates)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run 10 plain device copies of {COPY_CAL_MIB} MiB (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--pmc-by-grid", action="store_true",
+                    help="with --summarize-pmc: one row per kernel and grid size (for --sweep runs)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
-        return summarize_pmc(*args.summarize_pmc)
+        return summarize_pmc(*args.summarize_pmc, by_grid=args.pmc_by_grid)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
