@@ -11,6 +11,7 @@ next to this file.  Kernel resource usage (VGPR/AGPR/LDS/spills) is written to
 import argparse
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -73,6 +74,37 @@ def _link(objs, path, verbose):
         print(f"built {path}")
 
 
+def _resource_table(remarks):
+    """Markdown table of the compiler's per-kernel resource remarks (registers, scratch,
+    static LDS, occupancy); kernel names demangled with c++filt when it is there."""
+    rows, cur = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: +(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                      r"Occupancy \[waves/SIMD\]|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)", line)
+        if not m:
+            continue
+        key, val = m.groups()
+        if key == "Function Name":
+            cur = {"name": val}
+            rows.append(cur)
+        elif cur is not None:
+            cur[key] = val
+    names = [r["name"] for r in rows]
+    filt = shutil.which("c++filt")
+    if filt and names:
+        r = subprocess.run([filt], input="\n".join(names), capture_output=True, text=True)
+        if r.returncode == 0 and len(r.stdout.splitlines()) == len(names):
+            names = r.stdout.splitlines()
+    out = ["| kernel | VGPRs | AGPRs | SGPRs | spilled VGPRs | scratch bytes/lane | static LDS bytes | waves/SIMD |",
+           "|---|---|---|---|---|---|---|---|"]
+    for r, n in sorted(zip(rows, names), key=lambda x: x[1]):
+        n = n.replace("void ", "", 1).replace("fa355::(anonymous namespace)::", "").split("(")[0]
+        out.append("| `%s` | %s | %s | %s | %s | %s | %s | %s |" % (
+            n, r.get("VGPRs"), r.get("AGPRs"), r.get("TotalSGPRs"), r.get("VGPRs Spill"),
+            r.get("ScratchSize [bytes/lane]"), r.get("LDS Size [bytes/block]"), r.get("Occupancy [waves/SIMD]")))
+    return "\n".join(out) + "\n"
+
+
 def build(verbose=False):
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = SOURCES + MICRO_SOURCES
@@ -81,6 +113,8 @@ def build(verbose=False):
     usage = "\n".join(err for _, err in results.values() if "resource usage" in err.lower() or "remark" in err)
     with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
         f.write(usage)
+    with open(os.path.join(BUILD_DIR, "resource_usage.md"), "w") as f:
+        f.write(_resource_table(usage))
     _link([results[s][0] for s in SOURCES], LIB_PATH, verbose)
     _link([results[s][0] for s in MICRO_SOURCES], MICRO_LIB_PATH, verbose)
     return LIB_PATH
