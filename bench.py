@@ -21,8 +21,9 @@ Printed JSON line (rank 0 only):
   it; "machine": the bf16 MFMA, v_exp_f32, LDS-read and fp32-atomic rates the chip
   sustains, from the microbenchmark library), roofline (dominant launch, HIP events on
   the launch stream; "frac_of_sustained_mfma" is its rate against the measured MFMA
-  rate) and cpu_baseline (the fp64 oracle on a bounded sample, host cores of this
-  machine).
+  rate), cpu_baseline (the fp64 oracle on a bounded sample, host cores of this
+  machine) and env (device name, architecture, compute units, HBM size, torch and HIP
+  runtime versions).
 
 Options: --sweep prints one extra line per workload of the sweep to stderr.
 Profiling helpers (rocprofv3 runs whose summaries are committed under profiles/):
@@ -337,6 +338,15 @@ def run_machine(torch, dev, stream, reps=3):
     return res
 
 
+def run_env():
+    """Device and software the numbers were taken on."""
+    import torch
+
+    prop = torch.cuda.get_device_properties(0)
+    return {"device": prop.name, "arch": getattr(prop, "gcnArchName", None), "compute_units": prop.multi_processor_count,
+            "hbm_gib": round(prop.total_memory / 2**30, 1), "torch": torch.__version__, "hip_runtime": torch.version.hip}
+
+
 def _lib_handle():
     from exact_io_aware_19_amd import _lib
 
@@ -582,6 +592,7 @@ def main(argv=None):
         "detail": detail,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "env": run_env(),
     }
     print(json.dumps(line), flush=True)
     return 0
