@@ -417,6 +417,8 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
             res[direction] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                               "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                               "alg_gbs": round(_alg_bytes(B, H, N, d, direction, w.kv_heads) / (ms * 1e-3) / 1e9, 1)}
+        if name in ("tiny", "bert_large", "gpt2"):
+            res["step"] = time_step_graph(lib, torch, dev, t, w)
         if name.startswith("sweep_n") or name == "long_64k":
             # the FP8 forward on the same inputs (block quantisation + incoherent processing)
             res["fwd_fp8"] = {k: v for k, v in run_fp8(fa, wl, torch, dev, stream, t, w, iters)[
@@ -425,6 +427,60 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
         out.append(res)
         del t, o, lse
         torch.cuda.empty_cache()
+    return out
+
+
+def time_step_graph(lib, torch, dev, t, w, min_iters=20):
+    """One forward + backward step of a small workload, timed as back-to-back direct C-ABI
+    calls and as replays of a HIP graph that captured the same calls (the host cost of
+    launching is what differs at these sizes).  Both on one side stream with HIP events;
+    ms per step."""
+    B, H, N, d = w.shape
+    gs = torch.cuda.Stream(device=dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    ws = torch.empty(lib.fa_backward_gqa_workspace_size(B, H, w.kv_heads, N, d), dtype=torch.uint8, device=dev)
+    kvp = None if t["kv_len"] is None else t["kv_len"].data_ptr()
+    sp = gs.cuda_stream
+    fargs = (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+             w.kv_heads, N, d, w.scale, int(w.causal), kvp, sp)
+    bargs = (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), o.data_ptr(), t["do"].data_ptr(),
+             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, w.kv_heads, N, d, w.scale,
+             int(w.causal), kvp, ws.data_ptr(), ws.numel(), sp)
+
+    def step():
+        if lib.fa_forward_gqa(*fargs) != 0 or lib.fa_backward_gqa(*bargs) != 0:
+            raise RuntimeError("step launch failed")
+
+    gs.wait_stream(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        step()
+    torch.cuda.synchronize()
+    out = {}
+    for kind in ("eager", "graph"):
+        run = step if kind == "eager" else g.replay
+        with torch.cuda.stream(gs):
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run()
+            torch.cuda.synchronize()
+            n_it = max(min_iters, int(0.03 / max(time.perf_counter() - t0, 1e-6)))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(gs)
+            for _ in range(n_it):
+                run()
+            e1.record(gs)
+            torch.cuda.synchronize()
+        out[f"{kind}_ms"] = round(e0.elapsed_time(e1) / n_it, 4)
+    del g
     return out
 
 
