@@ -490,23 +490,32 @@ def cpu_baseline(inp, shape, heads):
     from oracle import ref
     from exact_io_aware_19_amd import workloads as wl
 
+    blas = None
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] + [1])
+        blas = ",".join(sorted({str(i.get("internal_api")) for i in info if i.get("user_api") == "blas"})) or None
     except Exception:  # threadpoolctl missing: numpy's BLAS default is one thread per core
         threads = os.cpu_count() or 1
     B, H, N, d = shape
     scale = 1.0 / math.sqrt(d)
     flops = 0.0
-    t0 = time.perf_counter()
+    t_fwd = t_bwd = 0.0
     for b, h in heads:
         qh, kh, vh, doh = (wl.bf16_bits_to_f64(getattr(inp, n)[b, h])[None, None] for n in ("q", "k", "v", "do"))
         for causal in (False, True):
+            t0 = time.perf_counter()
             ref.attention_forward(qh, kh, vh, scale, causal=causal)
+            t1 = time.perf_counter()
             ref.attention_backward(qh, kh, vh, doh, scale, causal=causal)
+            t2 = time.perf_counter()
+            t_fwd += t1 - t0
+            t_bwd += t2 - t1
             flops += 3.5 * fwd_flops(1, 1, N, d, causal)
-    sec = time.perf_counter() - t0
+    sec = t_fwd + t_bwd
+    scale_up = B * H / max(len(heads), 1)  # heads are independent: exact linear extrapolation
     return {
         "value": round(flops / sec / 1e12, 6),
         "unit": "TFLOP/s",
@@ -515,7 +524,11 @@ def cpu_baseline(inp, shape, heads):
         "sample": f"{len(heads)} of {B * H} heads of (B={B},H={H},N={N},d={d}), no mask and causal, "
                   f"forward+backward in numpy fp64; {sec:.1f} s",
         "seconds": round(sec, 2),
+        "forward_seconds": round(t_fwd, 2),
+        "backward_seconds": round(t_bwd, 2),
+        "full_step_seconds_extrapolated": round(sec * scale_up, 1),
         "host_cpus": os.cpu_count(),
+        "blas": blas,
     }
 
 
