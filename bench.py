@@ -335,6 +335,31 @@ def run_machine(torch, dev, stream, reps=3):
         ms = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
         res[key] = round(work / (ms * 1e-3) * unit, 1)
     res["mfma_bf16_pct_of_peak"] = round(100.0 * res["mfma_bf16_tflops"] / PEAK_BF16_TFLOPS, 1)
+    # MFMA and VALU streams of two waves on one SIMD (one 8-wave workgroup per CU): alone,
+    # then together; overlap = (mfma + valu - both) / min(mfma, valu), 1 = the shorter
+    # stream hidden entirely, 0 = the two serialised
+    lib.fa_micro_coexec.argtypes = [vp, i, i, i, i, i, vp]
+    lib.fa_micro_coexec.restype = i
+    cblocks = blocks // 2
+    cout = torch.empty(cblocks * 512, dtype=torch.float32, device=dev)
+    for kind, vk, v_iters in (("exp", 0, 30000), ("fma", 1, 80000)):
+        ms = {}
+        for mode, key in ((1, "mfma_ms"), (2, "valu_ms"), (3, "both_ms")):
+            def call():
+                return lib.fa_micro_coexec(cout.data_ptr(), cblocks, mode, vk, iters["mfma"], v_iters, sp)
+            if call() != 0:
+                raise RuntimeError(f"coexec {kind} mode {mode}: launch failed")
+            evs = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            ms[key] = round(sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2], 4)
+        ms["overlap"] = round((ms["mfma_ms"] + ms["valu_ms"] - ms["both_ms"]) / min(ms["mfma_ms"], ms["valu_ms"]), 3)
+        res[f"coexec_mfma_{kind}"] = ms
     return res
 
 

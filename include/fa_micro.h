@@ -49,6 +49,18 @@ int fa_micro_lds_read(float* out, int blocks, int iters, fa_stream_t stream);
  * holds ntiles * 8192 floats; blocks * tiles * 8192 atomic adds in total. */
 int fa_micro_atomic_tiles(float* buf, int ntiles, int blocks, int tiles, fa_stream_t stream);
 
+/* MFMA / VALU co-execution on one SIMD: workgroups of 512 threads (8 waves, one workgroup
+ * per compute unit; waves w and w + 4 share a SIMD).  mode 1: waves 0-3 run `mfma_iters`
+ * iterations of 8 independent v_mfma_f32_32x32x16_bf16 chains (as fa_micro_mfma_bf16);
+ * mode 2: waves 4-7 run `valu_iters` iterations of 16 independent per-lane chains,
+ * x <- exp2(-x) on v_exp_f32 (valu_kind 0) or x <- fma(x, 0.999, 1e-4) on v_fma_f32
+ * (valu_kind 1), from x0 = 0.25 + 0.03 k + 1e-6 (thread - 256); mode 3: both at once.
+ * `out` holds blocks * 512 floats: the MFMA waves' accumulator sums (0 when idle) and
+ * the VALU waves' chain sums (0 when idle).  Returns -1 for a NULL pointer, a count
+ * below 1 or a mode / valu_kind out of range. */
+int fa_micro_coexec(float* out, int blocks, int mode, int valu_kind, int mfma_iters, int valu_iters,
+                    fa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

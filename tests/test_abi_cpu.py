@@ -210,8 +210,8 @@ def test_micro_library_exports_every_declared_symbol():
         pytest.fail(f"{MICRO_LIB_PATH} not built; run python -m exact_io_aware_19_amd.build")
     with open(MICRO_HEADER) as f:
         names = sorted(set(re.findall(r"^\s*int\s+(fa_micro_\w+)\s*\(", f.read(), re.M)))
-    assert names == ["fa_micro_atomic_tiles", "fa_micro_exp", "fa_micro_grid_blocks", "fa_micro_lds_read",
-                     "fa_micro_mfma_bf16"]
+    assert names == ["fa_micro_atomic_tiles", "fa_micro_coexec", "fa_micro_exp", "fa_micro_grid_blocks",
+                     "fa_micro_lds_read", "fa_micro_mfma_bf16"]
     lib = ctypes.CDLL(MICRO_LIB_PATH)
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr), name
@@ -225,3 +225,7 @@ def test_micro_library_exports_every_declared_symbol():
     lib.fa_micro_atomic_tiles.argtypes = [vp, i, i, i, vp]
     assert lib.fa_micro_atomic_tiles(None, 1, 1, 1, None) == -1
     assert lib.fa_micro_atomic_tiles(vp(16), 0, 1, 1, None) == -1
+    lib.fa_micro_coexec.argtypes = [vp, i, i, i, i, i, vp]
+    for args in ((None, 1, 3, 0, 1, 1), (vp(16), 1, 0, 0, 1, 1), (vp(16), 1, 4, 0, 1, 1), (vp(16), 1, 3, 2, 1, 1),
+                 (vp(16), 1, 3, 0, 0, 1), (vp(16), 1, 3, 0, 1, 0), (vp(16), 0, 3, 0, 1, 1)):
+        assert lib.fa_micro_coexec(*args, None) == -1, args

@@ -106,3 +106,29 @@ def test_atomic_tiles_counts(gpu, micro):
             hits[(w + t) % ntiles] += 2
     got = buf.cpu().numpy().reshape(ntiles, 64 * 128)
     np.testing.assert_array_equal(got, np.repeat(hits[:, None], 64 * 128, axis=1).astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3])
+@pytest.mark.parametrize("valu_kind", [0, 1], ids=["exp", "fma"])
+def test_coexec_values(gpu, micro, mode, valu_kind):
+    # waves 0-3: the MFMA chains (sum 8 * 16 * iters * 2^-16 per lane) when mode bit 0 is
+    # set; waves 4-7: 16 chains per lane of exp2(-x) or fma(x, 0.999, 1e-4) when bit 1 is
+    import torch
+
+    P.say(f"micro coexec mode {mode} kind {valu_kind}")
+    micro.fa_micro_coexec.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    micro.fa_micro_coexec.restype = ctypes.c_int
+    blocks, it_m, it_v = 3, 30, 40
+    out = torch.full((blocks * 512,), -1.0, dtype=torch.float32, device=gpu)
+    assert micro.fa_micro_coexec(out.data_ptr(), blocks, mode, valu_kind, it_m, it_v, None) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(blocks, 512)
+    want_m = np.float32(8 * 16 * it_m * 2.0**-16) if mode & 1 else np.float32(0)
+    np.testing.assert_array_equal(got[:, :256], want_m)
+    if mode & 2:
+        x = 0.25 + 0.03 * np.arange(16)[:, None] + 1e-6 * np.arange(256)[None, :]
+        for _ in range(it_v):
+            x = np.exp2(-x) if valu_kind == 0 else x * 0.999 + 1e-4
+        np.testing.assert_allclose(got[:, 256:], np.tile(x.sum(axis=0), (blocks, 1)), rtol=2e-5, atol=0)
+    else:
+        np.testing.assert_array_equal(got[:, 256:], np.float32(0))
