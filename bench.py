@@ -595,17 +595,19 @@ def summarize_pmc(fetch_csv, write_csv, out_md, by_grid=False):
         out[counter] = {kname: sum(vs) / len(vs) for kname, vs in per.items()}
     m = re.search(r"--copy-calibration (\d+)", " ".join(sys.argv))
     sweep = " --sweep --no-machine" if by_grid else ""
-    tag = "_sweep" if by_grid else ""
+    fdir = os.path.relpath(os.path.dirname(os.path.abspath(fetch_csv)), ROOT)
+    wdir = os.path.relpath(os.path.dirname(os.path.abspath(write_csv)), ROOT)
     lines = [
         "# HBM traffic per launch, attention fwd/bwd, "
         + ("every workload of the sweep (one row per kernel and grid)" if by_grid else "B=2 H=16 N=8192 d=128"),
         "",
         "Commands (each on one MI355X, from the repository root, one counter per run):",
         "",
-        "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch%s -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration%s" % (tag, sweep),
-        "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write%s -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration%s" % (tag, sweep),
-        "    python bench.py --summarize-pmc%s gpurun_out/pmc_fetch%s/p_counter_collection.csv gpurun_out/pmc_write%s/p_counter_collection.csv %s"
-        % (" --pmc-by-grid" if by_grid else "", tag, tag, os.path.relpath(out_md, ROOT)),
+        "    rocprofv3 --pmc FETCH_SIZE -f csv -d %s -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration%s" % (fdir, sweep),
+        "    rocprofv3 --pmc WRITE_SIZE -f csv -d %s -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration%s" % (wdir, sweep),
+        "    python bench.py --summarize-pmc%s %s %s %s"
+        % (" --pmc-by-grid" if by_grid else "", os.path.relpath(os.path.abspath(fetch_csv), ROOT),
+           os.path.relpath(os.path.abspath(write_csv), ROOT), os.path.relpath(out_md, ROOT)),
         "",
         "Calibration: the last ten dispatches of the plain %d MiB device copy read and write" % COPY_CAL_MIB,
         "%d bytes each; the counters read %.0f KiB (FETCH_SIZE) and %.0f KiB (WRITE_SIZE)," % (COPY_CAL_MIB << 20, cal["FETCH_SIZE"], cal["WRITE_SIZE"]),
