@@ -25,7 +25,9 @@ Printed JSON line (rank 0 only):
   machine) and env (device name, architecture, compute units, HBM size, torch and HIP
   runtime versions).
 
-Options: --sweep prints one extra line per workload of the sweep to stderr.
+Options: --sweep prints one extra line per workload of the sweep to stderr (for the
+short-sequence workloads also a cold-cache time per call: median of single calls, each
+after overwriting 512 MiB so that neither the MALL nor an L2 holds the inputs).
 Profiling helpers (rocprofv3 runs whose summaries are committed under profiles/):
   --copy-calibration      also time a plain 256 MiB device copy (10 times), the
                           known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters
@@ -378,8 +380,12 @@ def _lib_handle():
     return _lib.load()
 
 
+COLD_WORKLOADS = ("tiny", "bert_large", "gpt2", "sweep_n2048_full", "sweep_n2048_causal")
+
+
 def run_sweep(fa, wl, torch, dev, stream, iters=10):
     out = []
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev).view(torch.float32)
     for name in ["tiny", "bert_large", "gpt2"] + [f"sweep_n{n}_{m}" for n in (2048, 4096, 8192, 16384)
                                                    for m in ("full", "causal")] + ["long_64k", "gqa_n8192",
                                                                                    "mqa_n4096"]:
@@ -442,6 +448,22 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
             res[direction] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                               "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                               "alg_gbs": round(_alg_bytes(B, H, N, d, direction, w.kv_heads) / (ms * 1e-3) / 1e9, 1)}
+            if name in COLD_WORKLOADS:
+                # cold caches: before each timed call, overwrite a buffer twice the size of
+                # the 256 MB MALL (and so every L2); the median of single-call event times
+                cold = []
+                for _ in range(11):
+                    flush.fill_(1.0)
+                    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    c0.record(stream)
+                    call()
+                    c1.record(stream)
+                    torch.cuda.synchronize()
+                    cold.append(c0.elapsed_time(c1))
+                cms = sorted(cold)[len(cold) // 2]
+                res[direction]["cold_ms"] = round(cms, 4)
+                res[direction]["cold_alg_gbs"] = round(
+                    _alg_bytes(B, H, N, d, direction, w.kv_heads) / (cms * 1e-3) / 1e9, 1)
         if name in ("tiny", "bert_large", "gpt2"):
             res["step"] = time_step_graph(lib, torch, dev, t, w)
         if name.startswith("sweep_n") or name == "long_64k":
