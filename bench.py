@@ -288,7 +288,8 @@ def run_machine(torch, dev, stream, reps=3):
     """Machine microbenchmarks (libfa355_micro.so, include/fa_micro.h), each launched
     `reps` times between HIP events on the bench stream; the median is reported.  They
     give what the chip sustains at its running clock: the bf16 MFMA rate, the v_exp_f32
-    rate, LDS read bandwidth and fp32 atomic-add throughput."""
+    rate, LDS read bandwidth, fp32 atomic-add throughput, and how far an MFMA stream and
+    a VALU stream of two waves on one SIMD overlap."""
     import ctypes
 
     from exact_io_aware_19_amd.build import MICRO_LIB_PATH

@@ -1,6 +1,6 @@
 // Microbenchmarks of the gfx950 units the attention kernels are bound by: the bf16 MFMA
 // rate the chip sustains (its clock under load included), the v_exp_f32 rate, LDS read
-// bandwidth and fp32 global atomic throughput.  They measure the machine, not attention:
+// bandwidth, fp32 global atomic throughput and MFMA/VALU co-execution on one SIMD.  They measure the machine, not attention:
 // the bench reports them beside the data-sheet peaks.  C ABI in include/fa_micro.h
 // (libfa355_micro.so, a library of its own).
 #include <hip/hip_runtime.h>
