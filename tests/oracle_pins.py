@@ -324,6 +324,48 @@ def pin_sampled_rows_match_full(ref, online):
             np.testing.assert_allclose(dqr, dq[b, 0, rows], rtol=0, atol=1e-13)
 
 
+def pin_row_chunks(ref, online):
+    """The oracle's row-chunked path (taken for long sequences) against torch float64
+    SDPA and autograd and against the single-chunk result, with chunks of 3 and 7 rows
+    over N = 20 and 37 (ragged last chunk), every mask mode, a positive and a negative
+    scale.  dK and dV are sums over all query chunks, so a chunk that overwrote instead
+    of accumulating, or rows not offset by the chunk start, fail here."""
+    import torch
+    import torch.nn.functional as F
+
+    saved = ref._ROW_CHUNK
+    try:
+        for seed, (N, d, scale) in enumerate([(20, 6, 0.45), (37, 5, -0.3)]):
+            for mode in MASK_MODES:
+                rng, q, k, v, do = _inputs(1450 + seed, 2, 2, N, d, with_do=True)
+                causal, kv = _mask_args(mode, rng, 2, N)
+                ref._ROW_CHUNK = saved
+                o1, l1 = ref.attention_forward(q, k, v, scale, causal=causal, kv_len=kv)
+                g1 = ref.attention_backward(q, k, v, do, scale, causal=causal, kv_len=kv)
+                for chunk in (3, 7):
+                    ref._ROW_CHUNK = chunk
+                    o, lse = ref.attention_forward(q, k, v, scale, causal=causal, kv_len=kv)
+                    g = ref.attention_backward(q, k, v, do, scale, causal=causal, kv_len=kv)
+                    np.testing.assert_allclose(o, o1, rtol=0, atol=1e-13)
+                    np.testing.assert_allclose(lse, l1, rtol=0, atol=1e-13)
+                    for a, b_ in zip(g, g1):
+                        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+                    for b in range(2):
+                        kl = None if kv is None else kv[b]
+                        m = _torch_mask(N, causal, kl)
+                        tq, tk, tv = (torch.from_numpy(x[b].copy()).requires_grad_(True) for x in (q, k, v))
+                        to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale)
+                        to.backward(torch.from_numpy(do[b]))
+                        np.testing.assert_allclose(o[b], to.detach().numpy(), rtol=0, atol=1e-12)
+                        s = (torch.matmul(tq, tk.transpose(-1, -2)) * scale).masked_fill(~m, float("-inf"))
+                        np.testing.assert_allclose(lse[b], torch.logsumexp(s, dim=-1).detach().numpy(), rtol=0,
+                                                   atol=1e-12)
+                        for a, tg in zip(g, (tq.grad, tk.grad, tv.grad)):
+                            np.testing.assert_allclose(a[b], tg.numpy(), rtol=0, atol=1e-11)
+    finally:
+        ref._ROW_CHUNK = saved
+
+
 def pin_online_equals_two_pass(ref, online):
     rng = _rng(1500)
     for N, d in [(1, 3), (17, 4), (64, 8)]:
@@ -412,6 +454,7 @@ ALL_PINS = [
     pin_permutation,
     pin_dk_columns_sum_to_zero,
     pin_sampled_rows_match_full,
+    pin_row_chunks,
     pin_online_equals_two_pass,
     pin_torch_sdpa_gqa,
     pin_gqa_identical_heads,

@@ -30,6 +30,12 @@ REF_MUTATIONS = {
     "dk_wrong_operand": ("dk += scale * (ds.T @ q[rows])", "dk += scale * (ds.T @ k[rows])"),
     "dv_p_not_transposed": ("dv += p.T @ dor", "dv += p @ dor"),
     "dp_uses_k": ("dp = dor @ v.T", "dp = dor @ k.T"),
+    "dk_chunk_overwrites": ("dk += scale * (ds.T @ q[rows])", "dk = scale * (ds.T @ q[rows])"),
+    "dv_chunk_overwrites": ("dv += p.T @ dor", "dv = p.T @ dor"),
+    "chunk_rows_not_offset": ("rows = np.arange(r0, min(N, r0 + _ROW_CHUNK))",
+                              "rows = np.arange(0, min(N, _ROW_CHUNK))"),
+    "chunk_last_rows_dropped": ("rows = np.arange(r0, min(n, r0 + _ROW_CHUNK))",
+                                "rows = np.arange(r0, min(n - 1, r0 + _ROW_CHUNK))"),
     "gqa_interleaved_heads": ("return attention_forward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)",
                               "return attention_forward(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1))"),
     "gqa_dk_not_summed": ("return dq, dk.reshape(B, Hkv, G, N, d).sum(axis=2)",
