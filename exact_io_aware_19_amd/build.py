@@ -63,6 +63,50 @@ def _compile(src, verbose):
     return obj, r.stderr
 
 
+# Sources whose kernels issue MFMAs as inline assembly (the compiler inserts no wait
+# states around those): their device assembly is checked after the build.
+ASM_CHECKED = ["fa_bwd.hip"]
+_MFMA_AGPR_B = re.compile(r"v_mfma_\S+\s+\S+,\s*\S+,\s*a\[(\d+):(\d+)\]")
+_AGPR_WRITE = re.compile(r"v_accvgpr_write_b32\s+a(\d+),")
+
+
+def check_inline_mfma_operands(asm_text, window=8):
+    """Find inline-asm MFMAs whose B operand (accumulation registers) was written by a
+    v_accvgpr_write among the `window` instructions before it.  The compiler does not
+    know an inline-asm product is an MFMA, so it inserts no wait states after such a
+    write and the product reads stale operands.  Returns the offending snippets."""
+    lines = asm_text.splitlines()
+    bad = []
+    for i, line in enumerate(lines):
+        m = _MFMA_AGPR_B.search(line)
+        if not m or i == 0 or "ASMSTART" not in lines[i - 1]:
+            continue
+        lo, hi = int(m.group(1)), int(m.group(2))
+        seen = 0
+        for j in range(i - 1, -1, -1):
+            t = lines[j].strip()
+            if not t or t.startswith(";") or t.startswith("."):
+                continue
+            seen += 1
+            if seen > window:
+                break
+            w = _AGPR_WRITE.search(t)
+            if w and lo <= int(w.group(1)) <= hi:
+                bad.append("\n".join(lines[j:i + 1]))
+                break
+    return bad
+
+
+def _device_asm(src):
+    out = os.path.join(BUILD_DIR, src + ".s")
+    cmd = [_hipcc(), *COMMON_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"device assembly of {src} failed:\n{r.stderr}")
+    with open(out) as f:
+        return f.read()
+
+
 def _link(objs, path, verbose):
     tmp = path + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
@@ -108,8 +152,14 @@ def _resource_table(remarks):
 def build(verbose=False):
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = SOURCES + MICRO_SOURCES
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs) + len(ASM_CHECKED)) as ex:
+        asm = {s: ex.submit(_device_asm, s) for s in ASM_CHECKED}
         results = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+        for s, fut in asm.items():
+            bad = check_inline_mfma_operands(fut.result())
+            if bad:
+                raise RuntimeError(f"{s}: {len(bad)} inline-asm MFMA(s) read accumulation registers written just "
+                                   f"before them (no wait states); first:\n{bad[0]}")
     usage = "\n".join(err for _, err in results.values() if "resource usage" in err.lower() or "remark" in err)
     with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
         f.write(usage)

@@ -51,7 +51,12 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 // results feed VALU code use these.  The compiler does not know these are MFMAs: a VALU
 // read of the result must come at least kMfmaValuWait wait states after the product
 // (callers insert them with mfma_valu_wait()); a following product may accumulate into
-// the result directly.
+// the result directly.  Nor does it insert the wait states a product needs after a VALU
+// write of its B operand: b_acc must be a value that lives in accumulation registers
+// (loaded there once, as the dK/dV pass's K and V fragments are).  A B operand computed
+// by VALU code (measured: K with its sign bits changed by an AND and an XOR) is kept in
+// vector registers and copied into accumulation registers right before each product,
+// which then reads stale values.
 constexpr int kMfmaValuWait = 12;  // 32x32x16 bf16 result -> VALU read, gfx950
 __device__ __forceinline__ f32x16 mfma32_vz(const u32x4& a, const u32x4& b_acc) {  // C = 0
   f32x16 d;
@@ -258,7 +263,9 @@ __device__ __forceinline__ uint32_t row_perm(uint32_t c) { return (c & ~12u) | (
 __device__ __forceinline__ constexpr int c_row(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
 
 // Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix (buffer resource `r`)
-// into a natural tile.  Rows past N are clamped to N-1 (finite data; callers mask them).
+// into a natural tile.  Rows at or past N are clamped to N-1: callers pass the number of
+// rows that may be read (the matrix length, or the key-padding limit), so rows beyond it
+// are never read and whatever they hold cannot reach a result (callers mask them).
 template <int ROWS, int D, int NWAVES>
 __device__ __forceinline__ void load_nat_tile(buf_rsrc r, int row0, int N, unsigned char* tile, int w, int l) {
   constexpr int NCH = D / 8;
@@ -351,8 +358,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* base, uint32
 // Direct copy of rows [row0, row0+ROWS) of a [N][D] bf16 matrix into a swizzled tile
 // (swz_unit, or swz4_unit if SWZ4), one wave instruction (1 KB) at a time: instruction ii of wave w fills the 64
 // consecutive 16-byte units starting at unit 64*(ii*NWAVES + w); the lane filling unit
-// u fetches the (row, chunk) that the swizzle places there.  Rows past N are clamped to
-// N-1 (finite data; callers give them zero weight).
+// u fetches the (row, chunk) that the swizzle places there.  Rows at or past N are clamped
+// to N-1 (callers pass the number of rows that may be read; rows beyond are never read
+// and get zero weight).
 template <int ROWS, int D, int NWAVES, bool SWZ4 = false>
 struct SwzCopy {
   static constexpr int NCH = D / 8;

@@ -25,7 +25,8 @@ int check_shape(int B, int H, int N, int d) {
   return FA_OK;
 }
 
-int check_scale(float scale) { return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE; }
+// any finite scale: negative and zero scales are carried by an operand's sign bits
+int check_scale(float scale) { return isfinite(scale) ? FA_OK : FA_ERR_SCALE; }
 
 int check_kv_heads(int H, int Hkv) { return (Hkv >= 1 && H % Hkv == 0) ? FA_OK : FA_ERR_KVHEADS; }
 
@@ -53,7 +54,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   a.Hkv = Hkv;
   a.N = N;
   a.d = d;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  const fa355::ScaleSign sg = fa355::scale_sign(scale, fa355::kSignBitsBf16);
+  a.scale_log2 = sg.scale_log2;
+  a.op_and = sg.op_and;
+  a.op_xor = sg.op_xor;
   a.causal = causal != 0;
   return fa355::launch_forward(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -108,7 +112,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   a.N = N;
   a.d = d;
   a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * 1.4426950408889634f;  // signed: no row maximum in the backward
   a.causal = causal != 0;
   a.nsplit = fa355::kv_splits(B, H, Hkv, N);
   a.part = (float*)((char*)workspace + stats_bytes(B, H, N));
@@ -229,7 +233,10 @@ int fa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, c
   a.H = H;
   a.N = N;
   a.d = d;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  const fa355::ScaleSign sg = fa355::scale_sign(scale, fa355::kSignBitsE4m3);
+  a.scale_log2 = sg.scale_log2;
+  a.op_and = sg.op_and;
+  a.op_xor = sg.op_xor;
   a.causal = causal != 0;
   return fa355::launch_forward_fp8(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -240,7 +247,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N < 1, or the problem is too large";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dim must be 64 or 128";
-    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite (post_scale finite and > 0)";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned (lse 4, workspace 256)";

@@ -133,8 +133,9 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
   auto issue = [&](int t, int s) {
 #pragma unroll
     for (int ii = 0; ii < Copy::PER_WAVE; ++ii) {
-      Copy::issue(kg, t * BN, N, kbuf(s), w, l, ii);
-      Copy::issue(vg, t * BN, N, vbuf(s), w, l, ii);
+      // rows at or past the last admissible key repeat it: padded rows are never read
+      Copy::issue(kg, t * BN, kv_end, kbuf(s), w, l, ii);
+      Copy::issue(vg, t * BN, kv_end, vbuf(s), w, l, ii);
     }
   };
 
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
 // elementwise work on the scores of one block runs between the dK^T, dV^T products of
 // the previous tile's block:
 //   step q:  S, dP (i+1, q)  then  dV^T, dK^T (i, q)  alongside  P, dS (i+1, q)
-// LDS: 2 x {Q, dO} natural, 2 x {Q^T, dO^T}, 2 x {lse2, D}.
+// LDS: 2 x {Q, dO} natural, 2 x {Q^T, dO^T}, 3 x {lse2, D}.
 // --------------------------------------------------------------------------------------
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = kKvWaves * 64;
@@ -284,8 +285,10 @@ struct KvLds {
   static constexpr int TILE = BM * D * 2;
   static constexpr int NAT = 0;         // slot s: Q at NAT + 2*s*TILE, dO right after
   static constexpr int TR = 4 * TILE;   // slot s: Q^T at TR + 2*s*TILE, dO^T right after
+  // row statistics of tile t in slot (t - first tile) % 3: iteration i reads those of
+  // tiles i and i+1 while the copy of tile i+2's lands, with no barrier in between
   static constexpr int ST = 8 * TILE;   // slot s: lse2[BM] at ST + 8*s*BM, D[BM] right after
-  static constexpr int BYTES = 8 * TILE + 2 * 8 * BM;
+  static constexpr int BYTES = 8 * TILE + 3 * 8 * BM;
 };
 
 // Compile-time placement of the P, dS groups in the dK/dV stream (see the kernel).  A
@@ -463,13 +466,14 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   const uint32_t t_rd = 16 * swz_unit<NCH>(8 * trc, tdc), t_wr = 16 * swz_unit<NCHT>(8 * tdc, trc);
   const bool t_dO = w >= 2;
 
-  // Direct copies of tile `it` into slot s: item k < 2*PER_WAVE is one 1 KB wave
-  // instruction of Q (k < PER_WAVE) or dO; item 2*PER_WAVE the row statistics (lse2 on
-  // even waves, D on odd ones; with BM = 64 waves 2-3 repeat what 0-1 copy).
+  // Direct copies of tile `it` into tile slot s and statistics slot ss: item k <
+  // 2*PER_WAVE is one 1 KB wave instruction of Q (k < PER_WAVE) or dO; item 2*PER_WAVE
+  // the row statistics (lse2 on even waves, D on odd ones; with BM = 64 waves 2-3
+  // repeat what 0-1 copy).
   using Copy = SwzCopy<BM, D, kKvWaves>;
   constexpr int PER_WAVE = Copy::PER_WAVE;
   constexpr int NDMA = 2 * PER_WAVE + 1;
-  auto dma_item = [&](int k, int it, int s) {
+  auto dma_item = [&](int k, int it, int s, int ss) {
     const int i0 = it * BM;
     if (k < PER_WAVE) {
       Copy::issue(qg, i0, N, nat_q(s), w, l, k);
@@ -478,12 +482,12 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     } else {
       constexpr int SW = BM / 64;  // wave instructions per statistic
       const int which = (w / SW) & 1, part = w % SW, row = i0 + part * 64 + l;
-      g2lds4((which ? wd : wl) + row, (which ? st_d(s) : st_l(s)) + part * 256);
+      g2lds4((which ? wd : wl) + row, (which ? st_d(ss) : st_l(ss)) + part * 256);
     }
   };
-  auto issue = [&](int it, int s) {
+  auto issue = [&](int it, int s, int ss) {
 #pragma unroll
-    for (int k = 0; k < NDMA; ++k) dma_item(k, it, s);
+    for (int k = 0; k < NDMA; ++k) dma_item(k, it, s, ss);
   };
   // tile `it` needs the causal mask for this wave iff some query precedes some key
   // P = exp2(S * scale * log2e - lse2) and dS = P * (dP - D) for two query rows
@@ -545,8 +549,8 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
 
   // ---- prologue: fetch tiles i_first and i_first+1, transpose and score i_first
   auto prologue = [&]() {
-  issue(i_first, 0);
-  issue(min(i_first + 1, i_last - 1), 1);
+  issue(i_first, 0, 0);
+  issue(min(i_first + 1, i_last - 1), 1, 1);
   wait_vmem();
   __syncthreads();
   transpose8x8(t_dO ? nat_d(0) : nat_q(0), t_rd, t_dO ? tr_d(0) : tr_q(0), t_wr);
@@ -585,6 +589,9 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   auto iteration = [&](auto PARc, auto MC, auto MS, int i) {
     constexpr int PAR = decltype(PARc)::value;
     const int cs = (i - i_first) & 1, ns = cs ^ 1;
+    // statistics slots of tiles i, i+1 (read here) and i+2 (copied here)
+    const int r3 = (i - i_first) % 3;
+    const int sc = r3, sn = r3 == 2 ? 0 : r3 + 1, s2 = r3 == 0 ? 2 : r3 - 1;
     const int it = i + 1, it2 = min(i + 2, i_last - 1);  // past the end: refetch, unused
     const unsigned char* t_src = t_dO ? nat_d(ns) : nat_q(ns);
     unsigned char* t_dst = t_dO ? tr_d(ns) : tr_q(ns);
@@ -602,8 +609,8 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
       constexpr int ua = Sch::unit_at(decltype(t_c)::value), n = Sch::seq(decltype(t_c)::value) % 3;
       constexpr bool carry = ua >= 1000;
       constexpr int q = carry ? NQB - 1 : ua / 16, u = carry ? ua - 1000 : ua % 16;
-      l2[n] = stat_pair(carry ? st_l(cs) : st_l(ns), stat_row(q, u));
-      dd[n] = stat_pair(carry ? st_d(cs) : st_d(ns), stat_row(q, u));
+      l2[n] = stat_pair(carry ? st_l(sc) : st_l(sn), stat_row(q, u));
+      dd[n] = stat_pair(carry ? st_d(sc) : st_d(sn), stat_row(q, u));
     };
     u32x4 fr[kLook];
 #pragma unroll
@@ -631,7 +638,7 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
         lds_write128(t_dst, t_wr ^ (16u * jj), y);
       }
       if constexpr (t >= 2 && (t - 2) % kDmaStep == 0 && (t - 2) / kDmaStep < NDMA)
-        dma_item((t - 2) / kDmaStep, it2, cs);
+        dma_item((t - 2) / kDmaStep, it2, cs, s2);
       if constexpr (t + 2 < T && Sch::unit_at(t + 2) >= 0)
         stat_read(std::integral_constant<int, t + 2>{}, sl2, sd2);
       // first read of block q's S, dP by VALU code: the products are inline assembly,
@@ -695,11 +702,11 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   };
   // last tile: carried groups, then its dV^T, dK^T products (set 0)
   auto epilogue = [&](auto MC, int i) {
-    const int cs = (i - i_first) & 1;
+    const int cs = (i - i_first) & 1, sc = (i - i_first) % 3;
 #pragma unroll
     for (int u = 4; u < 8; ++u)
-      group(MC, sbuf[(NQB - 1) & 1], dbuf[(NQB - 1) & 1], NQB - 1, u, stat_pair(st_l(cs), stat_row(NQB - 1, u)),
-            stat_pair(st_d(cs), stat_row(NQB - 1, u)), i, ps[0], dss[0]);
+      group(MC, sbuf[(NQB - 1) & 1], dbuf[(NQB - 1) & 1], NQB - 1, u, stat_pair(st_l(sc), stat_row(NQB - 1, u)),
+            stat_pair(st_d(sc), stat_row(NQB - 1, u)), i, ps[0], dss[0]);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -780,7 +787,15 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     else epilogue(F, i);
   }
   if (col_store) {
-    // keys padded away for every query get exact zeros
+    // keys padded away for every query get exact (+0) zeros: selected, not multiplied,
+    // since whatever a padded key row holds (inf, NaN) went into its accumulators
+    if (!col_live) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+      }
+    }
     if (nsplit > 1) {
       store_ct_rows_f32<D>(part_dk, kcol, dk, col_live ? p.scale : 0.f, h);
       store_ct_rows_f32<D>(part_dv, kcol, dv, col_live ? 1.f : 0.f, h);

@@ -313,7 +313,8 @@ __global__ __launch_bounds__(kThreads, 3) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
     for (int kk = 0; kk < NKK; ++kk) {
       const u32x4 lo = *(const u32x4*)(src + 64 * kk);
       const u32x4 hi = *(const u32x4*)(src + 64 * kk + 16);
-      qf[kk] = ok ? join8(lo, hi) : i32x8{};
+      // sign of the scale: E4M3 sign bits flipped (scale < 0) or codes zeroed (scale = 0)
+      qf[kk] = ok ? ((join8(lo, hi) & (int)p.op_and) ^ (int)p.op_xor) : i32x8{};
     }
   }
   // the wave's 32 rows lie in one 64-row scale block of Q

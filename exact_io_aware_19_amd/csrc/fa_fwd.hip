@@ -48,8 +48,10 @@ struct VtHalf {
     kc = part * (BN / 16) + (t >> 1) / (D / 4);
     k0 = kc * 8 + hsel * 4;
   }
-  __device__ __forceinline__ void fetch(buf_rsrc rs, int row0, int N) {
-    const int lim = N - 1 - row0;  // rows past N repeat row N-1 (finite; their P is 0)
+  // kend: one past the last admissible key; rows at or past it repeat row kend-1, so
+  // padded rows are never read (whatever they hold, their P is 0 and they add 0)
+  __device__ __forceinline__ void fetch(buf_rsrc rs, int row0, int kend) {
+    const int lim = kend - 1 - row0;
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (D * 2));  // wave-uniform
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = buf_load64(rs, (uint32_t)(min(k0 + j, lim) * (D * 2) + dq * 8), soff);
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
     const uint16_t* src = qg + (size_t)(ok ? qrow : 0) * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 t = *(const u32x4*)(src + 16 * kk);
-      qf[kk] = ok ? t : u32x4{0, 0, 0, 0};
+      const u32x4 t = *(const u32x4*)(src + 16 * kk);
+      qf[kk] = ok ? ((t & p.op_and) ^ p.op_xor) : u32x4{0, 0, 0, 0};  // sign of the scale
     }
   }
 
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   auto k_copy = [&](int row0, unsigned char* tile, int ii) {
     const int pos = (ii * 4 + wg) * 64 + l;  // unit index written by this lane
     const int blk = pos / (16 * (D / 8)), rem = pos % (16 * (D / 8));
-    const int row = min(blk * 16 + (rem & 15), N - 1 - row0);
+    const int row = min(blk * 16 + (rem & 15), kv_end - 1 - row0);  // padded rows never read
     // the LDS destination (M0) and the tile offset (soffset) are wave-uniform
     const int slot = __builtin_amdgcn_readfirstlane(ii * 4 + wg);
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (D * 2));
@@ -305,8 +307,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   // Both land before the barrier that ends phase 2j+3, in buffers whose previous
   // contents (V_{j-1}, K_j) were last read in phase 2j+1, so both rings are two deep.
   // V_0 is fetched here and written by MFMA operation -1 (phases 0 and 1).
-  load_nat_tile<BN, D, kWaves>(kg, 0, N, kbuf(0), w, l);
-  vh.fetch(vg, 0, N);
+  load_nat_tile<BN, D, kWaves>(kg, 0, kv_end, kbuf(0), w, l);
+  vh.fetch(vg, 0, kv_end);
   wait_vmem();
   __syncthreads();
   // operation index of group 0 in phase ph is ph, of group 1 is ph - 1:
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
     if (op >= 0) {
       if (op & 1) {
         const int j = op >> 1;
-        if (j + 1 < ntiles) vh.fetch(vg, (j + 1) * BN, N);
+        if (j + 1 < ntiles) vh.fetch(vg, (j + 1) * BN, kv_end);
         op_softmax(j);
         if (grp == 0) wait_vmem();
       } else {
@@ -399,8 +401,8 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
     const uint16_t* src = qg + (size_t)(ok ? qrow : 0) * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 t = *(const u32x4*)(src + 16 * kk);
-      qf[kk] = ok ? t : u32x4{0, 0, 0, 0};
+      const u32x4 t = *(const u32x4*)(src + 16 * kk);
+      qf[kk] = ok ? ((t & p.op_and) ^ p.op_xor) : u32x4{0, 0, 0, 0};  // sign of the scale
     }
   }
 
@@ -417,9 +419,9 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
   const uint32_t kfrag = NatFrag<D>::base(c, h);
   const uint32_t vfrag[2] = {TrFrag<BN>::base(c, h, 0), TrFrag<BN>::base(c, h, 1)};
 
-  load_nat_tile<BN, D, kW2>(kg, 0, N, kbuf(0), w, l);
-  vh[0].fetch(vg, 0, N);
-  vh[1].fetch(vg, 0, N);
+  load_nat_tile<BN, D, kW2>(kg, 0, kv_end, kbuf(0), w, l);
+  vh[0].fetch(vg, 0, kv_end);
+  vh[1].fetch(vg, 0, kv_end);
 #pragma unroll
   for (int c4 = 0; c4 < 4; ++c4) {
     vh[0].store(vbuf(0), c4);
@@ -430,9 +432,9 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
   for (int j = 0; j < ntiles; ++j) {
     const bool nxt = j + 1 < ntiles;
     if (nxt) {
-      load_nat_tile<BN, D, kW2>(kg, (j + 1) * BN, N, kbuf((j + 1) & 1), w, l);
-      vh[0].fetch(vg, (j + 1) * BN, N);
-      vh[1].fetch(vg, (j + 1) * BN, N);
+      load_nat_tile<BN, D, kW2>(kg, (j + 1) * BN, kv_end, kbuf((j + 1) & 1), w, l);
+      vh[0].fetch(vg, (j + 1) * BN, kv_end);
+      vh[1].fetch(vg, (j + 1) * BN, kv_end);
     }
     const int kt0 = j * BN;
     if (kt0 < wave_kend) {

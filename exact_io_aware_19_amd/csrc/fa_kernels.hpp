@@ -14,8 +14,10 @@ struct FwdArgs {
   const int32_t* kv_len;  // device int32[B] or nullptr
   int B, H, N, d;
   int Hkv;           // K/V heads; query head h reads K/V head h / (H / Hkv)
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // |scale| * log2(e) (log2(e) when scale = 0)
   int causal;
+  // sign of the scale, applied to every dword of the Q fragments: q = (q & op_and) ^ op_xor
+  uint32_t op_and, op_xor;
 };
 
 struct BwdArgs {
@@ -36,8 +38,11 @@ struct BwdArgs {
   int nw;
   int B, H, N, d;
   int Hkv;           // K/V heads; query head h reads K/V head h / (H / Hkv)
-  float scale;       // softmax scale
-  float scale_log2;  // scale * log2(e)
+  float scale;       // softmax scale (multiplies dQ and dK at the store)
+  // scale * log2(e), with its sign: the backward recomputes P = exp2(S * scale_log2 -
+  // LSE * log2(e)) from the saved LSE and needs no row maximum, so any finite scale
+  // (zero and negative included) enters as it is
+  float scale_log2;
   int causal;
   // grouped K/V heads with nsplit > 1: the query heads of a group are split over nsplit
   // workgroups per key block, which write fp32 partial dK, dV ([nsplit][B*Hkv][N][d]
@@ -72,9 +77,28 @@ struct Fp8FwdArgs {
   float* lse;
   const int32_t* kv_len;  // device int32[B] or nullptr
   int B, H, N, d;
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // |scale| * log2(e) (log2(e) when scale = 0)
   int causal;
+  uint32_t op_and, op_xor;  // sign of the scale, applied to every dword of the Q codes
 };
+
+// The kernels multiply scores by a positive factor only (the row maximum must commute
+// with scaling) and take the sign of the softmax scale from one operand held in
+// registers: for scale < 0 its sign bits are flipped (exact: -S = (-Q) K^T), for
+// scale = 0 it is zeroed (S = 0 exactly: uniform weights over the admissible keys).
+// `sign_bits` has the sign bit of every element of one dword set.
+struct ScaleSign {
+  float scale_log2;
+  uint32_t op_and, op_xor;
+};
+inline ScaleSign scale_sign(float scale, uint32_t sign_bits) {
+  constexpr float kLog2eHost = 1.4426950408889634f;
+  if (scale > 0.f) return {scale * kLog2eHost, 0xffffffffu, 0u};
+  if (scale < 0.f) return {-scale * kLog2eHost, 0xffffffffu, sign_bits};
+  return {kLog2eHost, 0u, 0u};
+}
+constexpr uint32_t kSignBitsBf16 = 0x80008000u;
+constexpr uint32_t kSignBitsE4m3 = 0x80808080u;
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_forward_fp8(const Fp8FwdArgs& a, hipStream_t stream);

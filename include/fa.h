@@ -26,7 +26,10 @@
  *    keys j < kv_len[b] are attended (values are clamped to [0, N]).  NULL = no padding.
  *  - causal != 0: query i attends keys j <= i (square problem, the same N for queries
  *    and keys).  Both masks may be combined.
- *  - scale must be finite and > 0 (it multiplies Q K^T before the softmax).
+ *  - scale is any finite float (it multiplies Q K^T before the softmax; the definition
+ *    on the pages puts no sign on it).  scale = 0 gives uniform weights over the
+ *    admissible keys (LSE = ln of their count, dQ = dK = 0); a negative scale favours
+ *    the smallest scores.  NaN and +-inf are rejected with FA_ERR_SCALE.
  *  - Supported head dims: d = 64 and d = 128.  Any N >= 1, B >= 1, H >= 1 with
  *    B*H*N*d < 2^62 and N*d*2 < 2^32 (one head's matrix below 4 GiB).
  *  - The caller owns every buffer.  The library never allocates, frees or
@@ -54,7 +57,7 @@ typedef enum {
   FA_ERR_NULL = -1,      /* a required pointer is NULL                          */
   FA_ERR_SHAPE = -2,     /* B, H or N < 1, or the element count overflows        */
   FA_ERR_HEADDIM = -3,   /* d is not 64 or 128                                   */
-  FA_ERR_SCALE = -4,     /* scale is not finite or not > 0                        */
+  FA_ERR_SCALE = -4,     /* scale is NaN or infinite (fp8 post_scale: also <= 0)  */
   FA_ERR_WORKSPACE = -5, /* backward workspace NULL or smaller than required     */
   FA_ERR_LAUNCH = -6,    /* a kernel launch failed (hipGetLastError)             */
   FA_ERR_ALIGN = -7,     /* a tensor pointer is not 16-byte aligned              */

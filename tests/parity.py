@@ -4,7 +4,8 @@ and compare with the fp64 oracle on the same seeded inputs.
 Tolerances (bf16 inputs, fp32 accumulation):
   O    max |err| <= 2e-2 and mean |err| <= 2e-3
   LSE  max |err| <= 1e-3
-  dQ, dK, dV relative Frobenius error <= 2e-2
+  dQ, dK, dV relative Frobenius error <= 2e-2, over the whole tensor and over every
+             64-row tile of every head
 """
 
 import sys
@@ -32,7 +33,7 @@ def to_np_bf16(t):
 
 def custom_inputs(B, H, N, d, seed, causal=False, kv_range=None, with_do=True, scale=None, scaled_key_frac=0.0,
                   h_kv=0):
-    w = wl.Workload(f"custom_{B}x{H}x{N}x{d}", B, H, N, d, causal, scale or 1.0 / np.sqrt(d), seed,
+    w = wl.Workload(f"custom_{B}x{H}x{N}x{d}", B, H, N, d, causal, 1.0 / np.sqrt(d) if scale is None else scale, seed,
                     kv_len_range=kv_range, scaled_key_frac=scaled_key_frac, backward=with_do, h_kv=h_kv)
     return wl.generate(w)
 
@@ -73,13 +74,40 @@ def rel_frob(g, ref_g):
     return float(num / den) if den > 0 else float(num)
 
 
+TILE_ROWS = 64
+
+
+def worst_tile(g, ref_g, rows=TILE_ROWS):
+    """Largest relative Frobenius error over the 64-row tiles of every head.
+
+    g, ref_g: [..., N, d].  A whole-tensor norm hides a single wrong row (one bad row of
+    a 16384-row head moves it by about 1e-2), so the same bound is also applied to every
+    tile of `rows` consecutive rows of each head.  A tile whose exact gradient is zero
+    (keys no query attends) is measured by its absolute error, which must then be 0 as
+    well.  Returns (error, (head index, first row))."""
+    n = g.shape[-2]
+    g2 = g.reshape(-1, n, g.shape[-1])
+    r2 = ref_g.reshape(-1, n, ref_g.shape[-1])
+    worst, where = 0.0, None
+    for hd in range(g2.shape[0]):
+        for r0 in range(0, n, rows):
+            e = rel_frob(g2[hd, r0:r0 + rows], r2[hd, r0:r0 + rows])
+            if e > worst or where is None:
+                worst, where = e, (hd, r0)
+    return worst, where
+
+
 def check_grads(grads_gpu, grads_ref, label=""):
-    out = {}
+    out, tiles = {}, {}
     for name, g, r in zip(("dq", "dk", "dv"), grads_gpu, grads_ref):
         gn = to_np_bf16(g) if not isinstance(g, np.ndarray) else g
         assert np.isfinite(gn).all(), f"{label}: {name} has non-finite values"
         out[name] = rel_frob(gn, r)
-    say(f"  {label}: rel-Frobenius dQ {out['dq']:.3e} dK {out['dk']:.3e} dV {out['dv']:.3e}")
+        tiles[name] = worst_tile(gn, r)
+    say(f"  {label}: rel-Frobenius dQ {out['dq']:.3e} dK {out['dk']:.3e} dV {out['dv']:.3e}; worst 64-row tile "
+        + " ".join(f"{n} {e:.3e}@{w}" for n, (e, w) in tiles.items()))
     for name, e in out.items():
         assert e <= GRAD_REL, (label, name, out)
+    for name, (e, w) in tiles.items():
+        assert e <= GRAD_REL, (label, name, "64-row tile", w, e)
     return out

@@ -56,8 +56,10 @@ def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, sc
         (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
         (dict(B=0), -2), (dict(H=0), -2), (dict(N=0), -2), (dict(N=-5), -2), (dict(B=1 << 20, H=1 << 11), -2),
         (dict(d=96), -3), (dict(d=0), -3), (dict(d=256), -3),
-        (dict(scale=0.0), -4), (dict(scale=-1.0), -4), (dict(scale=float("inf")), -4), (dict(scale=float("nan")), -4),
+        (dict(scale=float("inf")), -4), (dict(scale=float("-inf")), -4), (dict(scale=float("nan")), -4),
         (dict(q=FAKE + 8), -7), (dict(lse=FAKE + 2), -7),
+        # a zero or negative scale passes validation: the alignment error behind it is reported
+        (dict(scale=0.0, q=FAKE + 8), -7), (dict(scale=-1.0, q=FAKE + 8), -7), (dict(scale=-0.0, lse=FAKE + 2), -7),
     ],
 )
 def test_forward_rejects(lib, kw, status):
@@ -96,7 +98,10 @@ def test_backward_rejects_null(lib, missing):
 def test_backward_rejects_bad_args(lib):
     assert _bwd(lib, d=32) == -3
     assert _bwd(lib, N=0) == -2
-    assert _bwd(lib, scale=0.0) == -4
+    assert _bwd(lib, scale=float("nan")) == -4
+    assert _bwd(lib, scale=float("-inf")) == -4
+    assert _bwd(lib, scale=0.0, ws=FAKE + 16) == -7  # any finite scale is accepted
+    assert _bwd(lib, scale=-2.0, ws=FAKE + 16) == -7
     assert _bwd(lib, ws=None) == -5
     assert _bwd(lib, ws_bytes=16) == -5
     assert _bwd(lib, ws=FAKE + 16) == -7
@@ -132,7 +137,7 @@ def test_gqa_entry_points_reject_bad_kv_heads(lib, H, Hkv, status):
 def test_gqa_entry_points_validate_like_the_others(lib):
     assert lib.fa_forward_gqa(None, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, 0.125, 0, None, None) == -1
     assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 96, 0.125, 0, None, None) == -3
-    assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, 0.0, 0, None, None) == -4
+    assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, float("nan"), 0, None, None) == -4
     assert lib.fa_forward_gqa(FAKE, FAKE + 8, FAKE, FAKE, FAKE, 1, 4, 2, 16, 64, 0.1, 0, None, None) == -7
     need = lib.fa_backward_gqa_workspace_size(1, 4, 2, 16, 64)
 
@@ -173,8 +178,8 @@ def _fp8(lib, q8=FAKE, sq=FAKE, k8=FAKE, sk=FAKE, v8t=FAKE, sv=FAKE, o=FAKE, lse
     [
         (dict(q8=None), -1), (dict(sq=None), -1), (dict(k8=None), -1), (dict(sk=None), -1), (dict(v8t=None), -1),
         (dict(sv=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
-        (dict(N=0), -2), (dict(B=0), -2), (dict(d=96), -3), (dict(scale=0.0), -4), (dict(scale=float("nan")), -4),
-        (dict(q8=FAKE + 8), -7), (dict(v8t=FAKE + 4), -7), (dict(sk=FAKE + 2), -7), (dict(lse=FAKE + 1), -7),
+        (dict(N=0), -2), (dict(B=0), -2), (dict(d=96), -3), (dict(scale=float("inf")), -4), (dict(scale=float("nan")), -4),
+        (dict(scale=0.0, q8=FAKE + 8), -7), (dict(scale=-0.5, q8=FAKE + 8), -7), (dict(q8=FAKE + 8), -7), (dict(v8t=FAKE + 4), -7), (dict(sk=FAKE + 2), -7), (dict(lse=FAKE + 1), -7),
     ],
 )
 def test_forward_fp8_rejects(lib, kw, status):

@@ -322,3 +322,18 @@ def test_quantizers_bit_exact_extreme_values(gpu, d, rotate):
         assert sc.cpu().numpy()[0, 0, 1] == 0.0
         assert np.all(O.e4m3_decode(_u8(x8)[0, 0, 64:128]) == 0.0)
         assert np.all(_u8(x8)[0, 0, 64:70, :7] == 0x80)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125])
+def test_forward_fp8_any_finite_scale(gpu, scale):
+    """A zero or negative scale is carried by the Q codes (sign bits flipped or codes
+    zeroed), checked with the same per-element bound against the dequantised inputs."""
+    w = wl.get_workload("gpt2")
+    inp, t, shp, signs = _setup(gpu, w, (1, 2, 300, 64))
+    g = _quantize_gpu(gpu, t, shp, signs)
+    (q8, sq), (k8, sk), (v8, sv) = _quantize_oracle(inp, signs, shp[3])
+    of, lg = _run_forward(gpu, g, shp, scale, True)
+    qd, kd, vd = O.dequantize_blocks(q8, sq), O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
+    worst, rel, lerr = _check_forward(of, lg, qd, kd, vd, scale, True, None)
+    print(f"fp8 scale {scale}: max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  LSE {lerr:.2e}", flush=True)
+    assert worst <= 1.0 and rel <= 5e-2 and lerr <= 1e-3
