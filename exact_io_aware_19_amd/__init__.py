@@ -11,6 +11,10 @@ Low-level calls with the C names (caller allocates every output):
                 kv_len=None, stream=None)
     fa_backward_workspace_size(B, H, N, d)
     fa_backward_pass(which, ...)  # "dq" or "dkdv": the two passes of fa_backward
+    fa_backward_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len=None,
+                        stream=None)
+        no workspace: the library's own scratch (NOALLOC_SCRATCH_BYTES per GPU); calls
+        that overlap on one GPU race
     fa_forward_gqa(q, k, v, o, lse, scale, causal, kv_len=None, stream=None)
     fa_backward_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
                     kv_len=None, stream=None)
@@ -45,6 +49,8 @@ __all__ = [
     "fa_backward",
     "fa_backward_workspace_size",
     "fa_backward_pass",
+    "fa_backward_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "fa_forward_gqa",
     "fa_backward_gqa",
     "fa_backward_gqa_workspace_size",
@@ -59,6 +65,7 @@ __all__ = [
 ]
 
 FAError = _lib.FAError
+NOALLOC_SCRATCH_BYTES = _lib.NOALLOC_SCRATCH_BYTES
 
 
 def _torch():
@@ -207,6 +214,25 @@ def fa_backward_pass(which, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, wo
     if which not in ("dq", "dkdv"):
         raise ValueError("which must be 'dq' or 'dkdv'")
     _backward_call(which, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len, stream)
+
+
+def fa_backward_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len=None, stream=None):
+    """C ``fa_backward_noalloc``: fa_backward_kvlen without a workspace (the library's own
+    scratch array holds the row statistics); fills dq, dk, dv in place.  Problems whose
+    statistics exceed NOALLOC_SCRATCH_BYTES raise FAError (FA_ERR_WORKSPACE)."""
+    _check_qkv("q", q)
+    shape = tuple(q.shape)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_qkv(name, t, shape)
+    _check_lse(lse, shape)
+    B, H, N, d = shape
+    lib = _lib.load()
+    kvp = _kv_ptr(kv_len, B, q.device)
+    sp = _stream_ptr(stream, q.device)
+    st = lib.fa_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
+                                 int(bool(causal)), kvp, sp)
+    _lib.check(st, "fa_backward_noalloc")
 
 
 def _backward_call(which, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace, kv_len, stream):

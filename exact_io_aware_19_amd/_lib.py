@@ -11,6 +11,8 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libfa355.so")
 
 FA_OK = 0
+# include/fa.h: bytes of the library-owned scratch array of fa_backward_noalloc, per GPU
+NOALLOC_SCRATCH_BYTES = 16 << 20
 STATUS_NAMES = {
     0: "FA_OK",
     -1: "FA_ERR_NULL",
@@ -31,6 +33,7 @@ EXPORTED = (
     "fa_backward_kvlen",
     "fa_backward_dq_pass",
     "fa_backward_dkdv_pass",
+    "fa_backward_noalloc",
     "fa_forward_gqa",
     "fa_backward_gqa",
     "fa_backward_gqa_workspace_size",
@@ -68,6 +71,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
         fn.restype = i
+    lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    lib.fa_backward_noalloc.restype = i
     lib.fa_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
     lib.fa_forward_gqa.restype = i
     lib.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz, vp]

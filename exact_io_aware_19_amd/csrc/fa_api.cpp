@@ -5,10 +5,41 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_kernels.hpp"
 
 namespace {
+
+// Library-owned scratch of the allocation-free backward: the row statistics the dQ pass
+// writes and the dK/dV pass reads.  One copy per GPU, at its own address; host code
+// uses only the address looked up by scratch_address(), never the array's name.
+__device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the scratch array on the GPU of `stream` (the current GPU for the
+// null stream), looked up once per GPU with that GPU current.
+int scratch_address(fa_stream_t stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+  dev = cur;
+  if (stream && hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return FA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (e != hipSuccess || !ptr) return FA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
 
 int check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
@@ -169,6 +200,26 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
                        workspace_bytes_, stream);
 }
 
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                        int causal, const int32_t* kv_len, fa_stream_t stream) {
+  // every argument check of fa_backward_kvlen, and the size limit, before any HIP call
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if (workspace_bytes(B, H, H, N, d) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
+    return FA_ERR_ALIGN;
+  void* ws = nullptr;
+  st = scratch_address(stream, &ws);
+  if (st != FA_OK) return st;
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, kv_len, ws,
+                       (size_t)FA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int fa_backward_dq_pass(const void* q, const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                         int causal, const int32_t* kv_len, void* workspace, size_t workspace_bytes_,
@@ -248,7 +299,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N < 1, or the problem is too large";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dim must be 64 or 128";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite (post_scale finite and > 0)";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_WORKSPACE:
+      return "FA_ERR_WORKSPACE: workspace missing or too small (fa_backward_noalloc: problem beyond its scratch)";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned (lse 4, workspace 256)";
     case FA_ERR_KVHEADS: return "FA_ERR_KVHEADS: H_kv must be >= 1 and divide H";

@@ -128,6 +128,29 @@ int fa_backward_dkdv_pass(const void* q, const void* k, const void* v, const voi
                           fa_stream_t stream);
 
 /*
+ * Allocation-free backward, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results (bit for bit) and errors as fa_backward_kvlen (kv_len: device
+ * int32[B] or NULL), without the workspace: the row statistics the two passes exchange
+ * live in a device array owned by the library, FA_NOALLOC_SCRATCH_BYTES per GPU, held
+ * from the first call on that GPU until the process ends.  The call allocates and frees
+ * nothing.
+ *   - A problem whose statistics exceed the array (fa_backward_workspace_size(B, H, N, d)
+ *     > FA_NOALLOC_SCRATCH_BYTES, i.e. more than 2^21 padded rows B * H * ceil(N/256) *
+ *     256) returns FA_ERR_WORKSPACE before any HIP call.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on one GPU (on
+ *     different streams, or from several threads) race and may return wrong gradients.
+ *     Serialise them (one stream, or events).  Nothing in the array needs clearing
+ *     between calls: the dQ pass writes every entry the dK/dV pass reads.
+ *   - The first call on a GPU looks up the array's device address (hipGetSymbolAddress,
+ *     with that GPU current); a failure there returns FA_ERR_LAUNCH.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                        int causal, const int32_t* kv_len, fa_stream_t stream);
+
+/*
  * Grouped-query and multi-query attention (GQA, MQA): H query heads share H_kv K/V
  * heads, query head h using K/V head h / (H / H_kv) (groups of consecutive query
  * heads); H_kv = H is ordinary multi-head attention and H_kv = 1 is MQA.  The

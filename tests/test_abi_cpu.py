@@ -234,3 +234,28 @@ def test_micro_library_exports_every_declared_symbol():
     for args in ((None, 1, 3, 0, 1, 1), (vp(16), 1, 0, 0, 1, 1), (vp(16), 1, 4, 0, 1, 1), (vp(16), 1, 3, 2, 1, 1),
                  (vp(16), 1, 3, 0, 0, 1), (vp(16), 1, 3, 0, 1, 0), (vp(16), 0, 3, 0, 1, 1)):
         assert lib.fa_micro_coexec(*args, None) == -1, args
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=1, N=16, d=64,
+             scale=0.125, causal=0, kv=None)
+    a.update(kw)
+    return lib.fa_backward_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                   a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["kv"], None)
+
+
+def test_backward_noalloc_validates_before_any_hip_call(lib):
+    """Argument errors and the scratch limit (FA_NOALLOC_SCRATCH_BYTES = 16 MiB of row
+    statistics: 2^21 padded rows) are reported on the host, without a GPU."""
+    assert _lib.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert _noalloc(lib, dv=None) == -1
+    assert _noalloc(lib, N=0) == -2
+    assert _noalloc(lib, d=96) == -3
+    assert _noalloc(lib, scale=float("nan")) == -4
+    # 32 heads x 65536 rows = 2^21 rows fill the scratch exactly: accepted (the
+    # misaligned dq behind it is what gets reported); one more head is too many
+    assert lib.fa_backward_workspace_size(1, 32, 65536, 64) == _lib.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, H=32, N=65536, dq=FAKE + 4) == -7
+    assert _noalloc(lib, H=33, N=65536) == -5
+    assert _noalloc(lib, B=2, H=16, N=65537) == -5
+    assert _noalloc(lib, scale=-1.0, lse=FAKE + 2) == -7
