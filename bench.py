@@ -363,6 +363,26 @@ def run_machine(torch, dev, stream, reps=3):
             ms[key] = round(sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2], 4)
         ms["overlap"] = round((ms["mfma_ms"] + ms["valu_ms"] - ms["both_ms"]) / min(ms["mfma_ms"], ms["valu_ms"]), 3)
         res[f"coexec_mfma_{kind}"] = ms
+    # v_exp_f32 chains beside v_fma_f32 chains: on two waves of one SIMD (kind 2) and
+    # interleaved in one wave (kind 3); exp_ms / fma_ms alone, both_ms together
+    for name, vk in (("coexec_exp_fma_two_waves", 2), ("coexec_exp_fma_one_wave", 3)):
+        ms = {}
+        for mode, key in ((1, "exp_ms"), (2, "fma_ms"), (3, "both_ms")):
+            def call():
+                return lib.fa_micro_coexec(cout.data_ptr(), cblocks, mode, vk, 30000, 60000, sp)
+            if call() != 0:
+                raise RuntimeError(f"coexec {name} mode {mode}: launch failed")
+            evs = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            ms[key] = round(sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2], 4)
+        ms["overlap"] = round((ms["exp_ms"] + ms["fma_ms"] - ms["both_ms"]) / min(ms["exp_ms"], ms["fma_ms"]), 3)
+        res[name] = ms
     return res
 
 

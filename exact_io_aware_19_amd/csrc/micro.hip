@@ -88,50 +88,88 @@ __global__ __launch_bounds__(kMicroThreads) void atomic_tiles(float* __restrict_
 }
 
 // MFMA and VALU streams of different waves on one SIMD: 8-wave workgroups, one per CU,
-// waves w and w + 4 on the same SIMD.  Waves 0-3 run the MFMA chains of mfma_bf16_loop
-// (`mfma_iters` iterations) when mode bit 0 is set; waves 4-7 run 16 independent chains
-// per lane of `valu_iters` iterations when mode bit 1 is set: x <- exp2(-x) (valu_kind 0,
-// v_exp_f32) or x <- fma(x, 0.999, 1e-4) (valu_kind 1, v_fma_f32).  Timing the three
-// modes shows how far the two streams overlap.
+// waves w and w + 4 on the same SIMD.  valu_kind 0, 1: waves 0-3 run the MFMA chains of
+// mfma_bf16_loop (`mfma_iters` iterations) when mode bit 0 is set; waves 4-7 run 16
+// independent chains per lane of `valu_iters` iterations when mode bit 1 is set:
+// x <- exp2(-x) (valu_kind 0, v_exp_f32) or x <- fma(x, 0.999, 1e-4) (valu_kind 1,
+// v_fma_f32).  valu_kind 2 (transcendental beside FMA): waves 0-3 run the exp chains
+// (`mfma_iters` iterations, bit 0), waves 4-7 the FMA chains (`valu_iters`, bit 1).
+// valu_kind 3 (both in one wave): waves 0-3 run the exp chains (`mfma_iters`, bit 0) and
+// the FMA chains (`valu_iters`, bit 1) interleaved in one instruction stream; waves 4-7
+// idle.  Timing the three modes shows how far the two streams overlap.
 constexpr int kCoexThreads = 512;
+__device__ __forceinline__ void exp_chains(float (&x)[16], int iters) {
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = __builtin_amdgcn_exp2f(-x[k]);
+  }
+}
+__device__ __forceinline__ void fma_chains(float (&x)[16], int iters) {
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], 0.999f, 1e-4f);
+  }
+}
+__device__ __forceinline__ float chain_sum(const float (&x)[16]) {
+  float r = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) r += x[k];
+  return r;
+}
 __global__ __launch_bounds__(kCoexThreads, 1) void coexec_loop(float* __restrict__ out, int mode, int valu_kind,
                                                                int mfma_iters, int valu_iters) {
   const int tid = threadIdx.x, w = tid >> 6;
+  float* o = out + (size_t)blockIdx.x * kCoexThreads;
+  float x[16], y[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = y[k] = 0.25f + 0.03f * k + 1e-6f * (tid & 255);
+  if (valu_kind == 3) {  // one wave, both streams interleaved
+    if (w < 4) {
+      int i = 0;
+      if (mode == 3) {
+        const int n = min(mfma_iters, valu_iters);
+        for (; i < n; ++i) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            x[k] = __builtin_amdgcn_exp2f(-x[k]);
+            y[k] = __builtin_fmaf(y[k], 0.999f, 1e-4f);
+          }
+        }
+      }
+      if (mode & 1) exp_chains(x, mfma_iters - i);
+      if (mode & 2) fma_chains(y, valu_iters - i);
+      o[tid] = (mode & 1) ? chain_sum(x) : 0.f;
+      o[256 + tid] = (mode & 2) ? chain_sum(y) : 0.f;
+    }
+    return;
+  }
   float res = 0.f;
   if (w < 4) {
     if (mode & 1) {
-      const u32x4 a = {0x3A803A80u, 0x3A803A80u, 0x3A803A80u, 0x3A803A80u};
-      f32x16 acc[8];
+      if (valu_kind == 2) {
+        exp_chains(x, mfma_iters);
+        res = chain_sum(x);
+      } else {
+        const u32x4 a = {0x3A803A80u, 0x3A803A80u, 0x3A803A80u, 0x3A803A80u};
+        f32x16 acc[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = f32x16{};
-      for (int i = 0; i < mfma_iters; ++i) {
+        for (int k = 0; k < 8; ++k) acc[k] = f32x16{};
+        for (int i = 0; i < mfma_iters; ++i) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = mfma32(a, a, acc[k]);
+          for (int k = 0; k < 8; ++k) acc[k] = mfma32(a, a, acc[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) res += acc[k][r];
       }
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) res += acc[k][r];
     }
   } else if (mode & 2) {
-    float x[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) x[k] = 0.25f + 0.03f * k + 1e-6f * (tid - 256);
-    if (valu_kind == 0) {
-      for (int i = 0; i < valu_iters; ++i) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) x[k] = __builtin_amdgcn_exp2f(-x[k]);
-      }
-    } else {
-      for (int i = 0; i < valu_iters; ++i) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], 0.999f, 1e-4f);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) res += x[k];
+    if (valu_kind == 0) exp_chains(x, valu_iters);
+    else fma_chains(x, valu_iters);
+    res = chain_sum(x);
   }
-  out[(size_t)blockIdx.x * kCoexThreads + tid] = res;
+  o[tid] = res;
 }
 
 int cu_count() {
@@ -180,7 +218,7 @@ int fa_micro_atomic_tiles(float* buf, int ntiles, int blocks, int tiles, fa_stre
 
 int fa_micro_coexec(float* out, int blocks, int mode, int valu_kind, int mfma_iters, int valu_iters,
                     fa_stream_t stream) {
-  if (!out || blocks < 1 || mode < 1 || mode > 3 || valu_kind < 0 || valu_kind > 1 || mfma_iters < 1 ||
+  if (!out || blocks < 1 || mode < 1 || mode > 3 || valu_kind < 0 || valu_kind > 3 || mfma_iters < 1 ||
       valu_iters < 1)
     return -1;
   hipLaunchKernelGGL(fa355::coexec_loop, dim3(blocks), dim3(fa355::kCoexThreads), 0, (hipStream_t)stream, out, mode,

@@ -54,10 +54,17 @@ int fa_micro_atomic_tiles(float* buf, int ntiles, int blocks, int tiles, fa_stre
  * iterations of 8 independent v_mfma_f32_32x32x16_bf16 chains (as fa_micro_mfma_bf16);
  * mode 2: waves 4-7 run `valu_iters` iterations of 16 independent per-lane chains,
  * x <- exp2(-x) on v_exp_f32 (valu_kind 0) or x <- fma(x, 0.999, 1e-4) on v_fma_f32
- * (valu_kind 1), from x0 = 0.25 + 0.03 k + 1e-6 (thread - 256); mode 3: both at once.
+ * (valu_kind 1), from x0 = 0.25 + 0.03 k + 1e-6 (thread % 256); mode 3: both at once.
  * `out` holds blocks * 512 floats: the MFMA waves' accumulator sums (0 when idle) and
- * the VALU waves' chain sums (0 when idle).  Returns -1 for a NULL pointer, a count
- * below 1 or a mode / valu_kind out of range. */
+ * the VALU waves' chain sums (0 when idle).
+ * valu_kind 2 (transcendental beside FMA on one SIMD): waves 0-3 run the exp2 chains for
+ * `mfma_iters` iterations (mode bit 0) and waves 4-7 the FMA chains for `valu_iters`
+ * (bit 1); out: the exp chains' sums, then the FMA chains' sums.
+ * valu_kind 3 (both in one wave): waves 0-3 run the exp2 chains (`mfma_iters`, bit 0)
+ * and the FMA chains (`valu_iters`, bit 1) interleaved in one instruction stream, waves
+ * 4-7 idle; out[t] = exp chain sum of thread t < 256, out[256 + t] = its FMA chain sum
+ * (0 for a stream not run).
+ * Returns -1 for a NULL pointer, a count below 1 or a mode / valu_kind out of range. */
 int fa_micro_coexec(float* out, int blocks, int mode, int valu_kind, int mfma_iters, int valu_iters,
                     fa_stream_t stream);
 

@@ -108,6 +108,36 @@ def test_atomic_tiles_counts(gpu, micro):
     np.testing.assert_array_equal(got, np.repeat(hits[:, None], 64 * 128, axis=1).astype(np.float32))
 
 
+def _chains(kind, iters):
+    x = 0.25 + 0.03 * np.arange(16)[:, None] + 1e-6 * np.arange(256)[None, :]
+    for _ in range(iters):
+        x = np.exp2(-x) if kind == "exp" else x * 0.999 + 1e-4
+    return x.sum(axis=0)
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3])
+@pytest.mark.parametrize("valu_kind", [2, 3], ids=["exp_beside_fma", "exp_fma_one_wave"])
+def test_coexec_exp_fma_values(gpu, micro, mode, valu_kind):
+    # exp2 chains (mfma_iters iterations) and FMA chains (valu_iters) on two waves of one
+    # SIMD (kind 2) or interleaved in one wave (kind 3); out: exp sums, then FMA sums
+    import torch
+
+    P.say(f"micro coexec mode {mode} kind {valu_kind}")
+    micro.fa_micro_coexec.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    micro.fa_micro_coexec.restype = ctypes.c_int
+    blocks, it_e, it_f = 3, 30, 40
+    out = torch.full((blocks * 512,), -1.0, dtype=torch.float32, device=gpu)
+    assert micro.fa_micro_coexec(out.data_ptr(), blocks, mode, valu_kind, it_e, it_f, None) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(blocks, 512)
+    for half, bit, kind, it in ((0, 1, "exp", it_e), (1, 2, "fma", it_f)):
+        part = got[:, 256 * half:256 * (half + 1)]
+        if mode & bit:
+            np.testing.assert_allclose(part, np.tile(_chains(kind, it), (blocks, 1)), rtol=2e-5, atol=0)
+        else:
+            np.testing.assert_array_equal(part, np.float32(0))
+
+
 @pytest.mark.parametrize("mode", [1, 2, 3])
 @pytest.mark.parametrize("valu_kind", [0, 1], ids=["exp", "fma"])
 def test_coexec_values(gpu, micro, mode, valu_kind):
