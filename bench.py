@@ -115,15 +115,23 @@ def _quantile(xs, q):
     return ys[lo] + (ys[hi] - ys[lo]) * (pos - lo)
 
 
+def bench_workload(n):
+    """The large-head workload of the step: B=2, H=16, d=128, N=n, scale 1/sqrt(d), seeded
+    like the sweep's (the same inputs for both mask modes)."""
+    from exact_io_aware_19_amd import workloads as wl
+
+    return wl.Workload(f"sweep_n{n}", 2, 16, n, 128, False, 1.0 / math.sqrt(128), 1040 + int(math.log2(n)))
+
+
 def run_gpu(args):
     import torch
     import exact_io_aware_19_amd as fa
     from exact_io_aware_19_amd import workloads as wl
 
     dev = torch.device("cuda:0")
-    B, H, N, d = 2, 16, args.n, 128
-    scale = 1.0 / math.sqrt(d)
-    w = wl.Workload(f"sweep_n{N}", B, H, N, d, False, scale, 1040 + int(math.log2(N)))
+    w = bench_workload(args.n)
+    B, H, N, d = w.shape
+    scale = w.scale
     inp = wl.generate(w, with_do=True)
     t = inp.to_torch(dev)
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
@@ -552,51 +560,97 @@ def time_step_graph(lib, torch, dev, t, w, min_iters=20):
     return out
 
 
-def cpu_baseline(inp, shape, heads):
-    """The fp64 oracle as it stands, on `heads` (b, h) heads of the bench workload, both
-    mask modes, forward + backward; FLOPs counted with the same convention."""
+def _oracle_task_init():
+    """Worker initialiser of the CPU baseline: BLAS on one thread per worker process."""
+    try:
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(1)
+    except Exception:  # threadpoolctl missing: OPENBLAS_NUM_THREADS=1 was set before spawning
+        pass
+
+
+def _oracle_task(task):
+    """One task of the CPU baseline: the fp64 oracle's forward, then backward, of one head
+    under one mask mode.  Returns (forward seconds, backward seconds)."""
+    q_bits, k_bits, v_bits, do_bits, scale, causal = task
     from oracle import ref
     from exact_io_aware_19_amd import workloads as wl
 
+    qh, kh, vh, doh = (wl.bf16_bits_to_f64(x)[None, None] for x in (q_bits, k_bits, v_bits, do_bits))
+    t0 = time.perf_counter()
+    ref.attention_forward(qh, kh, vh, scale, causal=causal)
+    t1 = time.perf_counter()
+    ref.attention_backward(qh, kh, vh, doh, scale, causal=causal)
+    return t1 - t0, time.perf_counter() - t1
+
+
+def cpu_worker_count():
+    """One worker per host core this process may run on, at most 16 (the host share of one
+    GPU on the machines the bench runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(inp, shape, heads):
+    """The fp64 oracle as it stands, on `heads` (b, h) heads of the bench workload, both
+    mask modes, forward + backward, on a process pool of one single-threaded-BLAS worker
+    per host core; FLOPs counted with the same convention as the GPU line.  Must run
+    before this process touches the GPU: the workers are spawned (fresh interpreters)."""
+    import concurrent.futures
+    import multiprocessing
+
+    B, H, N, d = shape
+    scale = 1.0 / math.sqrt(d)
+    workers = cpu_worker_count()
+    tasks = [(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do[b, h], scale, causal)
+             for b, h in heads for causal in (False, True)]
+    flops = sum(3.5 * fwd_flops(1, 1, N, d, t[5]) for t in tasks)
+    saved = {k: os.environ.get(k) for k in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS")}
+    os.environ.update({k: "1" for k in saved})
+    try:
+        ctx = multiprocessing.get_context("spawn")
+        with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx,
+                                                    initializer=_oracle_task_init) as pool:
+            # start every worker and import the oracle before the clock starts
+            tiny = (inp.q[0, 0, :8], inp.k[0, 0, :8], inp.v[0, 0, :8], inp.do[0, 0, :8], scale, False)
+            list(pool.map(_oracle_task, [tiny] * workers))
+            t0 = time.perf_counter()
+            res = list(pool.map(_oracle_task, tasks))
+            wall = time.perf_counter() - t0
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    t_fwd = sum(r[0] for r in res)
+    t_bwd = sum(r[1] for r in res)
     blas = None
     try:
         from threadpoolctl import threadpool_info
 
-        info = threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] + [1])
-        blas = ",".join(sorted({str(i.get("internal_api")) for i in info if i.get("user_api") == "blas"})) or None
-    except Exception:  # threadpoolctl missing: numpy's BLAS default is one thread per core
-        threads = os.cpu_count() or 1
-    B, H, N, d = shape
-    scale = 1.0 / math.sqrt(d)
-    flops = 0.0
-    t_fwd = t_bwd = 0.0
-    for b, h in heads:
-        qh, kh, vh, doh = (wl.bf16_bits_to_f64(getattr(inp, n)[b, h])[None, None] for n in ("q", "k", "v", "do"))
-        for causal in (False, True):
-            t0 = time.perf_counter()
-            ref.attention_forward(qh, kh, vh, scale, causal=causal)
-            t1 = time.perf_counter()
-            ref.attention_backward(qh, kh, vh, doh, scale, causal=causal)
-            t2 = time.perf_counter()
-            t_fwd += t1 - t0
-            t_bwd += t2 - t1
-            flops += 3.5 * fwd_flops(1, 1, N, d, causal)
-    sec = t_fwd + t_bwd
-    scale_up = B * H / max(len(heads), 1)  # heads are independent: exact linear extrapolation
+        blas = ",".join(sorted({str(i.get("internal_api")) for i in threadpool_info() if i.get("user_api") == "blas"}))
+    except Exception:
+        pass
+    full_tasks = 2 * B * H  # every head, both mask modes: the whole step
     return {
-        "value": round(flops / sec / 1e12, 6),
+        "value": round(flops / wall / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{len(heads)} of {B * H} heads of (B={B},H={H},N={N},d={d}), no mask and causal, "
-                  f"forward+backward in numpy fp64; {sec:.1f} s",
-        "seconds": round(sec, 2),
-        "forward_seconds": round(t_fwd, 2),
-        "backward_seconds": round(t_bwd, 2),
-        "full_step_seconds_extrapolated": round(sec * scale_up, 1),
+        "sample": f"{len(heads)} of {B * H} heads of (B={B},H={H},N={N},d={d}), no mask and causal, forward+backward "
+                  f"in numpy fp64; {len(tasks)} tasks on {workers} single-threaded-BLAS worker processes; "
+                  f"{wall:.1f} s wall",
+        "seconds": round(wall, 2),
+        "worker_forward_seconds": round(t_fwd, 2),
+        "worker_backward_seconds": round(t_bwd, 2),
+        "full_step_seconds_extrapolated": round(wall * full_tasks / len(tasks), 1),
         "host_cpus": os.cpu_count(),
-        "blas": blas,
+        "blas": blas or None,
     }
 
 
@@ -678,7 +732,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=30, help="timed steps (default 30: about 200 ms of timed work)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--n", type=int, default=8192, help="sequence length of the bench workload (default 8192)")
-    ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="heads in the oracle CPU-baseline sample, each under both masks (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="also time every workload of the sweep (stderr)")
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the FP8 forward (timed after the bf16 step, reported under detail)")
@@ -698,6 +753,20 @@ def main(argv=None):
         print("bench.py measures one GPU only: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
+    # the CPU baseline first: its worker processes are spawned before this process
+    # initialises the GPU
+    cpu = None
+    if args.cpu_heads > 0:
+        import numpy as np
+
+        from exact_io_aware_19_amd import workloads as wl
+
+        inp = wl.generate(bench_workload(args.n), with_do=True)
+        rng = np.random.default_rng(12345)
+        B, H = inp.q.shape[:2]
+        heads = [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(args.cpu_heads)]
+        cpu = cpu_baseline(inp, inp.q.shape, heads)
+        del inp
     value, wall, detail, roofline, shape, inp, _ = run_gpu(args)
     B, H, N, d = shape
     if args.machine:
@@ -706,13 +775,6 @@ def main(argv=None):
         detail["machine"] = m = run_machine(torch, torch.device("cuda:0"), torch.cuda.current_stream())
         # the dominant kernel against the MFMA rate the chip sustains, beside the data-sheet peak
         roofline["frac_of_sustained_mfma"] = round(roofline["achieved"] / m["mfma_bf16_tflops"], 4)
-    cpu = None
-    if args.cpu_heads > 0:
-        import numpy as np
-
-        rng = np.random.default_rng(12345)
-        heads = [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(args.cpu_heads)]
-        cpu = cpu_baseline(inp, shape, heads)
     line = {
         "metric": METRIC,
         "value": round(value, 2),

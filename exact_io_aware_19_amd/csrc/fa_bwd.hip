@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
       auto pair = [&](auto kbp_c) {  // interior tiles only: no mask
         constexpr int KA = 2 * decltype(kbp_c)::value;
         constexpr int NSP = 2 * NKK, NQ = 2 * NDB, T = 2 * NSP + 2 * NQ;
-        constexpr int kLook = 2;
+        // one product ahead: two waves share each SIMD and hide each other's operand
+        // reads; reading two ahead needed 6 more registers than the 256 the two waves
+        // allow (spilled) and measured no faster
+        constexpr int kLook = 1;
         f32x16 sc[2], dp[2];
         u32x4 dsk[2][2];
         // op t: [0, NSP) S/dP of a, [NSP, 2NSP) S/dP of b, then dQ of a, dQ of b

@@ -231,7 +231,7 @@ def test_micro_library_exports_every_declared_symbol():
     assert lib.fa_micro_atomic_tiles(None, 1, 1, 1, None) == -1
     assert lib.fa_micro_atomic_tiles(vp(16), 0, 1, 1, None) == -1
     lib.fa_micro_coexec.argtypes = [vp, i, i, i, i, i, vp]
-    for args in ((None, 1, 3, 0, 1, 1), (vp(16), 1, 0, 0, 1, 1), (vp(16), 1, 4, 0, 1, 1), (vp(16), 1, 3, 2, 1, 1),
+    for args in ((None, 1, 3, 0, 1, 1), (vp(16), 1, 0, 0, 1, 1), (vp(16), 1, 4, 0, 1, 1), (vp(16), 1, 3, 4, 1, 1), (vp(16), 1, 3, -1, 1, 1),
                  (vp(16), 1, 3, 0, 0, 1), (vp(16), 1, 3, 0, 1, 0), (vp(16), 0, 3, 0, 1, 1)):
         assert lib.fa_micro_coexec(*args, None) == -1, args
 

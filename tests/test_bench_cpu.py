@@ -111,3 +111,18 @@ def test_traffic_figure_is_dropped_when_the_sources_change(tmp_path, monkeypatch
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_cpu_baseline_runs_a_spawned_single_threaded_pool():
+    """The CPU baseline leg on a small sample: one spawned worker per host core (at most
+    16), each with single-threaded BLAS, both mask modes per head; the line's fields."""
+    import bench
+    from exact_io_aware_19_amd import workloads as wl
+
+    w = wl.Workload("small", 1, 2, 256, 64, False, 0.125, 77)
+    inp = wl.generate(w, with_do=True)
+    out = bench.cpu_baseline(inp, inp.q.shape, [(0, 0), (0, 1)])
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s" and out["value"] > 0
+    assert out["cores"] == bench.cpu_worker_count() <= 16
+    assert "4 tasks" in out["sample"]
+    assert out["full_step_seconds_extrapolated"] == round(out["seconds"] * 4 / 4, 1)
