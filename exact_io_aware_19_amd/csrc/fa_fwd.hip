@@ -34,43 +34,6 @@ constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr float kRescaleTau = 8.0f;
 constexpr int kLdsTiles = 4;  // 2 K tiles + 2 V^T tiles
 
-// Register-staged transposition of one half of a V tile (rows [BN/2 * part, +BN/2)) by
-// the 256 threads of one wave group: each thread moves one 4x4 bf16 block (4 keys x 4
-// head-dim columns) into the transposed [D][BN] tile, one 8-byte column at a time.
-template <int BN, int D>
-struct VtHalf {
-  static_assert((BN / 2 / 4) * (D / 4) == 256, "one 4x4 block per thread of a wave group");
-  u32x2 r[4];
-  int k0, dq, kc, hsel;
-  __device__ __forceinline__ void init(int t, int part) {
-    hsel = t & 1;
-    dq = (t >> 1) % (D / 4);
-    kc = part * (BN / 16) + (t >> 1) / (D / 4);
-    k0 = kc * 8 + hsel * 4;
-  }
-  // kend: one past the last admissible key; rows at or past it repeat row kend-1, so
-  // padded rows are never read (whatever they hold, their P is 0 and they add 0)
-  __device__ __forceinline__ void fetch(buf_rsrc rs, int row0, int kend) {
-    const int lim = kend - 1 - row0;
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (D * 2));  // wave-uniform
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = buf_load64(rs, (uint32_t)(min(k0 + j, lim) * (D * 2) + dq * 8), soff);
-  }
-  // column j of the block: (V[k0 .. k0+3][4*dq + j])
-  __device__ __forceinline__ void store(unsigned char* tile, int j) const {
-    const int half = j >> 1;
-    u32x2 out;
-    if (j & 1) {
-      out[0] = hi16_pair(r[0][half], r[1][half]);
-      out[1] = hi16_pair(r[2][half], r[3][half]);
-    } else {
-      out[0] = lo16_pair(r[0][half], r[1][half]);
-      out[1] = lo16_pair(r[2][half], r[3][half]);
-    }
-    lds_write64(tile, bcm_tr_byte<BN / 8>(dq * 4 + j, kc) + hsel * 8, out);
-  }
-};
-
 template <int D, int BN, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
