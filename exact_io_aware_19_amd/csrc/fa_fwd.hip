@@ -32,7 +32,76 @@ constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
 // optimisation; wiki page, FA4 (2)): the reference max moves only when a row max grows
 // by more than this, so un-normalised probabilities stay below 2^8.
 constexpr float kRescaleTau = 8.0f;
+constexpr float kRescaleLimit = 256.0f;  // 2^kRescaleTau
 constexpr int kLdsTiles = 4;  // 2 K tiles + 2 V^T tiles
+
+// P = exp2(s * scale * log2e - m_ref) of one lane's 16*NKB scores of a tile, packed to
+// bf16 pairs (the B operand of O^T += V^T P^T); returns the lane's share of the tile's
+// row sum, from the unrounded fp32 P (the log-sum-exp the backward recomputes P from
+// must be accurate to fp32, not to bf16), as a tree (a serial chain would leave the
+// VALU idle between dependent issues).
+template <int NKB>
+__device__ __forceinline__ float tile_probs(const f32x16 (&s)[NKB], float sl, float m_ref, u32x4 (&pk)[NKB][2]) {
+  float t[8 * NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * sb + 2 * i], sl, -m_ref));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * sb + 2 * i + 1], sl, -m_ref));
+        pk[kb][sb][i] = pack_bf16x2(p0, p1);
+        t[8 * kb + 4 * sb + i] = p0 + p1;
+      }
+#pragma unroll
+  for (int n = 4 * NKB; n >= 1; n >>= 1)
+#pragma unroll
+    for (int i = 0; i < n; ++i) t[i] = t[i] + t[i + n];
+  return t[0];
+}
+
+// Online-softmax step of one tile for one wave: P of the tile's (masked) scores s into
+// pk, and the row state -- reference max m_run in scaled-log2 units, this lane's partial
+// row sum l_run, output accumulators o -- updated.  Conditional rescaling
+// (FlashAttention-4 summary, second optimisation; wiki page, FA4 (2)): the reference
+// moves only when some row max exceeds it by more than tau; results are exact for any
+// reference (it cancels in O and is added back in the LSE) and tau bounds the
+// un-normalised P by 2^tau.
+//   GATED (the 8-wave kernel, whose softmax runs in a phase of its own): P is first
+//   formed against the current reference; each P is at most its lane's share of the
+//   tile sum, so when no share exceeds 2^tau (and every row has a reference) the
+//   reference stays, P is final and the row max (a tree of three-input maxima over the
+//   raw scores, which s still holds) is not needed; otherwise it decides as below.
+//   Not gated (the small-grid kernel, whose products follow in the same wave and
+//   overlap the exponentials): row max first, then P.
+// Both give the same P, sums and outputs; they can differ only where P = 2^tau lies
+// within rounding of the threshold, where either reference is exact.
+template <bool GATED, int NKB, int NDB>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], float sl, float& m_run, float& l_run,
+                                             f32x16 (&o)[NDB], u32x4 (&pk)[NKB][2]) {
+  float lt = 0.f;
+  if constexpr (GATED) {
+    lt = tile_probs<NKB>(s, sl, (m_run == -INFINITY) ? 0.f : m_run, pk);
+    if (!__any(!(lt <= kRescaleLimit) || m_run == -INFINITY)) {
+      l_run += lt;
+      return;
+    }
+  }
+  float mx = tree_max<NKB>(s);
+  mx = half_max(mx) * sl;
+  const bool moved = __any(mx > m_run + kRescaleTau);
+  if (moved) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+  }
+  if (!GATED || moved) lt = tile_probs<NKB>(s, sl, (m_run == -INFINITY) ? 0.f : m_run, pk);
+  l_run += lt;
+}
 
 template <int D, int BN, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
@@ -225,35 +294,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
           s[kb][r] = bad ? -INFINITY : s[kb][r];
         }
     }
-    // row max and row sum are reduced as trees: in this phase the wave has the VALU to
-    // itself, so a serial 32-long dependency chain would leave it idle between issues
-    float mx = tree_max<NKB>(s);
-    mx = half_max(mx) * sl;
-    // The reference max only moves when some row of the wave grew by more than tau:
-    // results are exact for any reference (it cancels in O and is added back in the
-    // LSE); tau bounds the un-normalised P by 2^tau.
-    if (__any(mx > m_run + kRescaleTau)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], sl, -m_use));
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[kb][sb][i] = pack_bf16x2(s[kb][8 * sb + 2 * i], s[kb][8 * sb + 2 * i + 1]);
-    // the row sum uses the unrounded fp32 P: the log-sum-exp the backward recomputes P
-    // from must be accurate to fp32, not to bf16
-    l_run += tree_sum<NKB>(s);
+    softmax_tile<true, NKB, NDB>(s, sl, m_run, l_run, o, pk);
   };
 
   // ---- phase schedule ---------------------------------------------------------------
@@ -427,29 +468,8 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
             s[kb][r] = bad ? -INFINITY : s[kb][r];
           }
       }
-      float mx = tree_max<NKB>(s);
-      mx = half_max(mx) * sl;
-      if (__any(mx > m_run + kRescaleTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], sl, -m_use));
       u32x4 pk[NKB][2];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pk[kb][sb][i] = pack_bf16x2(s[kb][8 * sb + 2 * i], s[kb][8 * sb + 2 * i + 1]);
-      l_run += tree_sum<NKB>(s);
+      softmax_tile<false, NKB, NDB>(s, sl, m_run, l_run, o, pk);
       const unsigned char* vb_ = vbuf(j & 1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)

@@ -79,7 +79,7 @@ int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Size in bytes of the device workspace fa_backward needs: two fp32 per query row,
- * D_i = sum_k dO_ik O_ik and LSE_i * log2(e), for N rounded up to a multiple of 256
+ * -D_i (D_i = sum_k dO_ik O_ik) and LSE_i * log2(e), for N rounded up to a multiple of 256
  * rows per head: 8 * B * H * (256 * ceil(N / 256)) bytes.  dQ needs no accumulator: it
  * is produced by a query-outer pass that keeps its rows in registers.  Returns 0 for
  * invalid sizes.
@@ -112,7 +112,7 @@ int fa_backward_kvlen(const void* q, const void* k, const void* v, const void* o
  * followed by fa_backward_dkdv_pass(args) on the same stream.  Arguments, validation
  * and error codes are those of fa_backward_kvlen (kv_len: device int32[B] or NULL for
  * no padding).
- *   fa_backward_dq_pass:   writes dq and the row statistics D_i and LSE_i * log2(e)
+ *   fa_backward_dq_pass:   writes dq and the row statistics -D_i and LSE_i * log2(e)
  *                          into the workspace (dk, dv are not touched);
  *   fa_backward_dkdv_pass: reads those statistics and writes dk and dv (dq is not
  *                          touched); it must follow a dQ pass on the same inputs and
