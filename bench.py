@@ -687,8 +687,9 @@ def summarize_pmc(fetch_csv, write_csv, out_md, by_grid=False):
         for _, name, v in rows:
             if "fa355" in name:
                 key = name.replace("void ", "", 1) if name.startswith("void ") else name
-                key = key.replace("fa355::(anonymous namespace)::", "").split("(")[0]
-                per.setdefault(key, []).append(v)
+                key = key.replace("fa355::(anonymous namespace)::", "").replace("fa355::", "").split("(")[0]
+                if key.startswith(("fa_", "fp8_")):  # attention kernels, not the machine microbenchmarks
+                    per.setdefault(key, []).append(v)
         out[counter] = {kname: sum(vs) / len(vs) for kname, vs in per.items()}
     m = re.search(r"--copy-calibration (\d+)", " ".join(sys.argv))
     sweep = " --sweep --no-machine" if by_grid else ""

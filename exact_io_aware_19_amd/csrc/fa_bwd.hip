@@ -118,6 +118,25 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
     return;
   }
   const float sl = p.scale_log2;
+  // -D of this lane's query four times over in LDS (16 bytes per query row, a region per
+  // wave after the tiles): four 16-byte reads of it fill a dP^T accumulator, so the dP^T
+  // products yield dP^T - D directly, with no subtraction per score (volatile: four
+  // reads into the accumulator's registers, not one read and twelve register copies)
+  unsigned char* const ndt = smem + 4 * TILE_BYTES + w * 32 * 16;
+  if (h == 0) {
+    const uint32_t nd = __builtin_bit_cast(uint32_t, -di);
+    lds_write128(ndt, 16 * c, u32x4{nd, nd, nd, nd});
+  }
+  auto neg_d = [&]() {
+    f32x16 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 v = *(const volatile lds_u32x4*)((const __attribute__((address_space(3))) unsigned char*)ndt + 16 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = __builtin_bit_cast(float, (uint32_t)v[e]);
+    }
+    return x;
+  };
   // Fragment bases.  S^T, dP^T: lane (c, h) reads K / V row 32*kb + row_perm(c), chunk
   // 2*kk + h; the swizzle depends on kk only through kk % 2.  dQ^T: the K^T operand
   // (rows d = 32*db + c, k-slots keys 16*sb + 8*h + 0..7 of block kb) comes from two
@@ -157,6 +176,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
       // fragments read kLook products ahead:
       //   S, dP (a) | S, dP (b) with P, dS (a) between the products | dQ (a) with P, dS (b)
       //   between them | dQ (b)
+      // (each block's S products before its dP products, which start from -D)
       // so the elementwise work of one block overlaps the other block's products.
       auto pair = [&](auto kbp_c) {  // interior tiles only: no mask
         constexpr int KA = 2 * decltype(kbp_c)::value;
@@ -169,9 +189,9 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
         u32x4 dsk[2][2];
         // op t: [0, NSP) S/dP of a, [NSP, 2NSP) S/dP of b, then dQ of a, dQ of b
         auto aread = [&](int t) -> u32x4 {
-          if (t < 2 * NSP) {
-            const int kb = KA + t / NSP, r = t % NSP, kk = r >> 1;
-            return lds_read128((r & 1) ? vbuf(cur) : kbuf(cur), nb[kk & 1] + kb * 2 * BLK16 + (kk >> 1) * 64 * 16);
+          if (t < 2 * NSP) {  // S products of a block, then its dP products
+            const int kb = KA + t / NSP, r = t % NSP, kk = r % NKK;
+            return lds_read128((r >= NKK) ? vbuf(cur) : kbuf(cur), nb[kk & 1] + kb * 2 * BLK16 + (kk >> 1) * 64 * 16);
           }
           const int u = t - 2 * NSP, kb = KA + u / NQ, m = u % NQ, sb = m / NDB, db = m % NDB;
           const uint32_t off = (2 * kb + sb) * BLK16 + db * 4 * 16 * 16;
@@ -183,7 +203,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
           const int sb = g >> 2, e = g & 3, r0 = 8 * sb + 2 * e;
           const float p0 = fast_exp2(__builtin_fmaf(sc[x][r0], sl, -lse2));
           const float p1 = fast_exp2(__builtin_fmaf(sc[x][r0 + 1], sl, -lse2));
-          dsk[x][sb][e] = pack_bf16x2(p0 * (dp[x][r0] - di), p1 * (dp[x][r0 + 1] - di));
+          dsk[x][sb][e] = pack_bf16x2(p0 * dp[x][r0], p1 * dp[x][r0 + 1]);
         };
         u32x4 fr[kLook];
 #pragma unroll
@@ -194,12 +214,13 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
           if constexpr (t + kLook < T) fr[t % kLook] = aread(t + kLook);
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (t < 2 * NSP) {
-            constexpr int x = t / NSP, r = t % NSP, kk = r >> 1;
-            if constexpr (r & 1) dp[x] = mfma32(a, dof[kk], kk == 0 ? f32x16{} : dp[x]);
+            constexpr int x = t / NSP, r = t % NSP, kk = r % NKK;
+            if constexpr (r == 0) dp[x] = neg_d();  // lands before the block's dP products
+            if constexpr (r >= NKK) dp[x] = mfma32(a, dof[kk], dp[x]);
             else sc[x] = mfma32(a, qf[kk], kk == 0 ? f32x16{} : sc[x]);
-            // P, dS of block a: its eight groups spread over the dP products of block b
-            if constexpr (x == 1 && (r & 1)) {
-              constexpr int G0 = (8 * kk) / NKK, G1 = (8 * (kk + 1)) / NKK;
+            // P, dS of block a: its eight groups spread over the products of block b
+            if constexpr (x == 1) {
+              constexpr int G0 = (8 * r) / NSP, G1 = (8 * (r + 1)) / NSP;
               static_for<G1 - G0>([&](auto gc) { group(0, G0 + decltype(gc)::value); });
             }
           } else {
@@ -221,7 +242,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
         // edge tiles (causal diagonal, padding, ragged end): one block at a time
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          f32x16 s = f32x16{}, dp = f32x16{};
+          f32x16 s = f32x16{}, dp = neg_d();
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk) {
             const uint32_t off = nb[kk & 1] + kb * 2 * BLK16 + (kk >> 1) * 64 * 16;
@@ -242,7 +263,7 @@ __global__ __launch_bounds__(kDqThreads) void fa_bwd_dq_kernel(BwdArgs p) {
               }
               const float p0 = bad0 ? 0.f : fast_exp2(__builtin_fmaf(s[r0], sl, -lse2));
               const float p1 = bad1 ? 0.f : fast_exp2(__builtin_fmaf(s[r0 + 1], sl, -lse2));
-              dsk[sb][e] = pack_bf16x2(p0 * (dp[r0] - di), p1 * (dp[r0 + 1] - di));
+              dsk[sb][e] = pack_bf16x2(p0 * dp[r0], p1 * dp[r0 + 1]);
             }
 #pragma unroll
           for (int sb = 0; sb < 2; ++sb)
@@ -860,7 +881,7 @@ template <int D, int BN, int BM, bool CAUSAL, bool KVLEN>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, int passes) {
   const unsigned bh = (unsigned)(a.B * a.H);
   if (passes & 1) {
-    constexpr size_t lds = 4ull * BN * D * 2;
+    constexpr size_t lds = 4ull * BN * D * 2 + kDqWaves * 32 * 16;
     auto kern = fa_bwd_dq_kernel<D, BN, CAUSAL, KVLEN>;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
