@@ -213,6 +213,14 @@ __device__ __forceinline__ void buf2lds16(buf_rsrc r, uint32_t voff, uint32_t so
       r, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) unsigned char*)lds_wave_base),
       16, voff, soff, 0, 0);
 }
+// 4 bytes per lane straight into LDS at lds_wave_base + 4*lane (a buffer load: unlike a
+// global one it counts only in the vector-memory wait counter, so waits for earlier LDS
+// reads can stay partial)
+__device__ __forceinline__ void buf2lds4(buf_rsrc r, uint32_t voff, uint32_t soff, unsigned char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) unsigned char*)lds_wave_base),
+      4, voff, soff, 0, 0);
+}
 __device__ __forceinline__ u32x2 buf_load64(buf_rsrc r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
@@ -377,13 +385,6 @@ struct SwzCopy {
   }
 };
 
-// 4 bytes per lane straight into LDS at lds_wave_base + 4*lane.
-__device__ __forceinline__ void g2lds4(const void* gptr, unsigned char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void*)gptr,
-                                   (__attribute__((address_space(3))) void*)(
-                                       (__attribute__((address_space(3))) unsigned char*)lds_wave_base),
-                                   4, 0, 0);
-}
 
 // Transposition of one 8x8 bf16 block between swizzled tiles: rows 8*rc .. 8*rc+7,
 // chunk dc of a natural [R][D] tile become rows 8*dc .. 8*dc+7, chunk rc of the

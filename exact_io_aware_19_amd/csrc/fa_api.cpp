@@ -97,7 +97,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 int workspace_rows(int N) { return (N + 255) / 256 * 256; }
 
 size_t stats_bytes(int B, int H, int N) {
-  // D_i and LSE_i * log2(e), fp32 [B][H][nw] each (a multiple of 2 KiB: the partials
+  // -D_i and LSE_i * log2(e), fp32 [B][H][nw] each (a multiple of 2 KiB: the partials
   // that follow stay 256-byte aligned)
   return 2 * (size_t)B * H * workspace_rows(N) * 4;
 }

@@ -18,7 +18,7 @@
 // reproducible.
 //
 //   launch 1  fa_bwd_dq_kernel    (query-outer, 8 waves x 32 query rows)
-//             D_i = rowsum(dO * O) -> workspace;  S^T = K Q^T, dP^T = V dO^T,
+//             D_i = rowsum(dO * O), -D_i -> workspace;  S^T = K Q^T, dP^T = V dO^T,
 //             dS^T = P^T * (dP^T - D);  dQ^T += K^T dS^T
 //   launch 2  fa_bwd_dkdv_kernel  (key-outer, 4 waves x 32 key columns)
 //             S = Q K^T, dP = dO V^T, dS = P * (dP - D);
@@ -417,15 +417,13 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
   float* const part_dk = GROUPED ? p.part + ((size_t)split * BHkv + bhk) * N * D : nullptr;
   float* const part_dv = GROUPED ? part_dk + (size_t)nsplit * BHkv * N * D : nullptr;
   const size_t head = (size_t)bhk * N * D;          // K, V, dK, dV
-  buf_rsrc qg, dog;
-  const float* __restrict__ wl;
-  const float* __restrict__ wd;
+  buf_rsrc qg, dog, wlg, wdg;
   auto set_query_head = [&](int g) {
     const size_t qhead = (size_t)(bq0 + g) * N * D;
     qg = make_rsrc(p.q + qhead, (uint32_t)N * D * 2);
     dog = make_rsrc(p.dout + qhead, (uint32_t)N * D * 2);
-    wl = p.ws_l + (size_t)(bq0 + g) * p.nw;
-    wd = p.ws_d + (size_t)(bq0 + g) * p.nw;
+    wlg = make_rsrc(p.ws_l + (size_t)(bq0 + g) * p.nw, (uint32_t)p.nw * 4);
+    wdg = make_rsrc(p.ws_d + (size_t)(bq0 + g) * p.nw, (uint32_t)p.nw * 4);
   };
   set_query_head(g_begin);
 
@@ -508,7 +506,7 @@ __global__ __launch_bounds__(kKvThreads) void fa_bwd_dkdv_kernel(BwdArgs p) {
     } else {
       constexpr int SW = BM / 64;  // wave instructions per statistic
       const int which = (w / SW) & 1, part = w % SW, row = i0 + part * 64 + l;
-      g2lds4((which ? wd : wl) + row, (which ? st_d(ss) : st_l(ss)) + part * 256);
+      buf2lds4(which ? wdg : wlg, (uint32_t)row * 4, 0, (which ? st_d(ss) : st_l(ss)) + part * 256);
     }
   };
   auto issue = [&](int it, int s, int ss) {

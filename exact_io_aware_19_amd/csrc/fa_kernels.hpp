@@ -33,7 +33,7 @@ struct BwdArgs {
   const int32_t* kv_len;  // device int32[B] or nullptr
   // workspace, written by the dQ pass and read by the dK/dV pass, per head nw rows
   // (N rounded up to 256; rows past N hold D = 0, lse2 = +inf):
-  float* ws_d;  // D_i = rowsum(dO * O), fp32 [B][H][nw]
+  float* ws_d;  // -D_i, D_i = rowsum(dO * O), fp32 [B][H][nw]
   float* ws_l;  // LSE_i * log2(e), +inf where the row has no admissible key, fp32 [B][H][nw]
   int nw;
   int B, H, N, d;
