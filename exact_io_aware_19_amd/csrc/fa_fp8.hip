@@ -42,6 +42,7 @@ constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
 // the row's main terms out of E4M3's subnormal range (below 2^-6).
 constexpr float kTau = 4.0f;
 constexpr float kBias = 4.0f;
+constexpr float kPLimit = 256.0f;  // 2^(kTau + kBias)
 
 // fp8 x fp8 -> fp32, 32x32x64.  Operand layout (probed on gfx950): lane l supplies row
 // (A) or column (B) l % 32 and contraction slots 32*(l/32) .. +31, one per byte; C as
@@ -407,30 +408,44 @@ __global__ __launch_bounds__(kThreads, 3) void fa_fwd_fp8_kernel(Fp8FwdArgs p) {
             s[kb][r] = bad ? -INFINITY : s[kb][r];
           }
       }
-      float mx = tree_max<2>(s);
-      mx = half_max(mx) * sl;
-      if (__any(mx > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      }
-      const float m_use = ((m_run == -INFINITY) ? 0.f : m_run) - kBias;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], sl, -m_use));
       // P^T as the B operand: byte p of half h is key pv_key(h, p) = register p % 16 of
-      // score block p / 16
+      // score block p / 16.  P is first formed against the current reference; each P is
+      // at most its lane's share of the tile sum, so when no share exceeds 2^(kTau +
+      // kBias) (and every row has a reference) the reference stays and the row max is
+      // not needed; otherwise the row max over the raw scores (s keeps them) decides as
+      // usual.  The sum runs in four partial chains, which keeps the registers within the
+      // budget of three waves per SIMD.
       i32x8 pk;
+      auto probs = [&](float m_ref) {
+        const float m_use = m_ref - kBias;
+        float t[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kb = i >> 2, r0 = 4 * (i & 3);
-        pk[i] = (int)pack_fp8x4(s[kb][r0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3]);
+        for (int i = 0; i < 8; ++i) {
+          const int kb = i >> 2, r0 = 4 * (i & 3);
+          float e[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) e[x] = fast_exp2(__builtin_fmaf(s[kb][r0 + x], sl, -m_use));
+          pk[i] = (int)pack_fp8x4(e[0], e[1], e[2], e[3]);
+          const float q = (e[0] + e[1]) + (e[2] + e[3]);
+          t[i & 3] = i < 4 ? q : t[i & 3] + q;
+        }
+        return (t[0] + t[1]) + (t[2] + t[3]);
+      };
+      float lt = probs((m_run == -INFINITY) ? 0.f : m_run);
+      if (__any(!(lt <= kPLimit) || m_run == -INFINITY)) {
+        float mx = tree_max<2>(s);
+        mx = half_max(mx) * sl;
+        if (__any(mx > m_run + kTau)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+          lt = probs((m_run == -INFINITY) ? 0.f : m_run);
+        }
       }
-      l_run += tree_sum<2>(s);
+      l_run += lt;
       // O^T += V_j^T P^T
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
