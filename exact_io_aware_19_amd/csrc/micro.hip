@@ -179,6 +179,33 @@ int cu_count() {
   return n;
 }
 
+
+// One v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit scales) on one wave: C = A B^T
+// + C0 for A, B of 32 rows x 64 bytes (row-major codes) and C0, C of 32 x 32 floats
+// (row-major).  Operand layout: lane l supplies row l % 32 of A (and of B) and
+// contraction slots 32 (l / 32) .. +31, one per byte; the accumulator element r of lane l
+// is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  Used to read the accumulation precision
+// of the fp8 product.
+typedef int i32x8m __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(64) void mfma_fp8_tile(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                    const float* __restrict__ c0, float* __restrict__ c) {
+  const int l = threadIdx.x, row = l & 31, h = l >> 5;
+  const uint32_t* ar = reinterpret_cast<const uint32_t*>(a + row * 64 + 32 * h);
+  const uint32_t* br = reinterpret_cast<const uint32_t*>(b + row * 64 + 32 * h);
+  i32x8m av, bv;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    av[k] = (int)ar[k];
+    bv[k] = (int)br[k];
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = c0[(8 * (r >> 2) + 4 * h + (r & 3)) * 32 + row];
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c[(8 * (r >> 2) + 4 * h + (r & 3)) * 32 + row] = acc[r];
+}
+
 }  // namespace
 }  // namespace fa355
 
@@ -223,6 +250,13 @@ int fa_micro_coexec(float* out, int blocks, int mode, int valu_kind, int mfma_it
     return -1;
   hipLaunchKernelGGL(fa355::coexec_loop, dim3(blocks), dim3(fa355::kCoexThreads), 0, (hipStream_t)stream, out, mode,
                      valu_kind, mfma_iters, valu_iters);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int fa_micro_mfma_fp8_tile(const void* a, const void* b, const float* c0, float* c, fa_stream_t stream) {
+  if (!a || !b || !c0 || !c) return -1;
+  hipLaunchKernelGGL(fa355::mfma_fp8_tile, dim3(1), dim3(64), 0, (hipStream_t)stream, (const uint8_t*)a,
+                     (const uint8_t*)b, c0, c);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

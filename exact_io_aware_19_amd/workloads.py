@@ -30,6 +30,7 @@ __all__ = [
     "f32_to_bf16_bits",
     "bf16_bits_to_f64",
     "generate",
+    "staircase",
     "fp8_signs",
 ]
 
@@ -152,6 +153,27 @@ class Inputs:
             out["do"] = t(self.do)
         out["kv_len"] = None if self.kv_len is None else torch.from_numpy(self.kv_len.astype(np.int32)).to(device)
         return out
+
+
+def staircase(B, H, N, d, rise, seed, causal=False, block=64):
+    """Inputs whose scores climb along the keys: q = (1, e), k = (rise * (j // block) /
+    scale, e'), with e, e' ~ 0.1 N(0, 1) in the other d - 1 dimensions and scale =
+    1/sqrt(d), so that the scaled score of key j grows by about `rise` (natural-log units)
+    per block of keys.  Every block raises the row maximum: by less than the rescaling
+    threshold, by more, or (large rises) by more than the fp32 exponent range of
+    un-normalised probabilities.  v, dO ~ N(0, 1).  Draw order: e, e', v, dO."""
+    scale = 1.0 / math.sqrt(d)
+    w = Workload(f"staircase_{B}x{H}x{N}x{d}_{rise:g}", B, H, N, d, causal, scale, seed, backward=True,
+                 note="scores rising by a fixed amount per block of keys")
+    rng = np.random.default_rng(seed)
+    qf = 0.1 * rng.standard_normal((B, H, N, d), dtype=np.float32)
+    kf = 0.1 * rng.standard_normal((B, H, N, d), dtype=np.float32)
+    vf = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    dof = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    qf[..., 0] = 1.0
+    kf[..., 0] = (rise / scale) * (np.arange(N, dtype=np.float32) // block)
+    return Inputs(workload=w, q=f32_to_bf16_bits(qf), k=f32_to_bf16_bits(kf), v=f32_to_bf16_bits(vf),
+                  do=f32_to_bf16_bits(dof))
 
 
 def generate(w, with_do=None, shape_override=None):

@@ -68,6 +68,12 @@ int fa_micro_atomic_tiles(float* buf, int ntiles, int blocks, int tiles, fa_stre
 int fa_micro_coexec(float* out, int blocks, int mode, int valu_kind, int mfma_iters, int valu_iters,
                     fa_stream_t stream);
 
+/* Accumulation precision of the fp8 matrix product: one v_mfma_scale_f32_32x32x64_f8f6f4
+ * (OCP E4M3 codes for both operands, unit scales) on one wave, C = A B^T + C0.  a and b
+ * hold 32 x 64 E4M3 codes row-major (row i of b is column i of B), c0 and c 32 x 32
+ * floats row-major; all four are device pointers.  One 64-thread workgroup. */
+int fa_micro_mfma_fp8_tile(const void* a, const void* b, const float* c0, float* c, fa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,16 @@ relative Frobenius error of O to stay below 5e-2: E4M3's relative rounding error
 RMS of about 2^-4 / sqrt(3) ~ 3.6% per P element, and O's error is a p-weighted average of
 such errors on random-sign values, of the same relative size as O.
 LSE uses the unrounded P and must match to 1e-3 like the bf16 path.
+
+The scores carry one more error: the fp8 matrix product does not sum its 64 products in
+full fp32 precision.  Measured on gfx950 (tests/test_gpu_micro.py, which also asserts
+it), the sum of one 32x32x64 product is off by at most 2^-11.8 of its largest |term|,
+also when that term cancels; fp32 would be within 2^-18.  So each score may be off by
+    delta_i = 2^-10 * scale * max_k |q_ik| * max_j,k |k_jk|   (dequantised; 3.6x margin)
+which bounds the LSE error by delta_i and moves every P by a factor within e^(+-2 delta_i):
+the tests allow |dLSE_i| <= 1e-3 + delta_i and add (e^(2 delta_i) - 1) sum_j p_ij |v_jc|
+to the bound on O.  For inputs of unit size delta is a few 1e-4; it matters where one
+product dominates a score of hundreds (tests/test_gpu_rescale.py).
 """
 
 import math
@@ -94,8 +104,9 @@ def test_quantizers_bit_exact(gpu, name, shape, rotate):
 
 
 def _check_forward(o_gpu, lse_gpu, qd, kd, vd, scale, causal, kv_len, rows=None):
-    """Compare GPU rows with the oracle on the dequantised inputs, using the bound of the
-    module docstring; returns (max |dO| / bound, O rel. Frobenius error, max |dLSE|)."""
+    """Compare GPU rows with the oracle on the dequantised inputs, using the bounds of the
+    module docstring; returns (max |dO| / bound, O rel. Frobenius error, max |dLSE| /
+    (1e-3 + delta)) -- the last is at most 1 when LSE is within its bound."""
     B, H, N, d = qd.shape
     worst, num, den, lerr = 0.0, 0.0, 0.0, 0.0
     for b in range(B):
@@ -110,13 +121,20 @@ def _check_forward(o_gpu, lse_gpu, qd, kd, vd, scale, causal, kv_len, rows=None)
             lse = m[:, 0] + np.log(e.sum(axis=1))
             p = e / e.sum(axis=1, keepdims=True)
             o = p @ vd[b, h]
-            bound = 2.0 ** -4 * (p @ np.abs(vd[b, h])) + 2.0 ** -14 * (ok @ np.abs(vd[b, h])) + \
+            kmax = np.abs(kd[b, h]).max(axis=1)
+            kmax_adm = np.where(ok, kmax[None, :], 0.0).max(axis=1) if ok.shape[1] else np.zeros(len(r))
+            delta = 2.0 ** -10 * abs(scale) * np.abs(qd[b, h, r]).max(axis=1) * kmax_adm
+            pv = p @ np.abs(vd[b, h])
+            bound = 2.0 ** -4 * pv + np.expm1(2 * delta)[:, None] * pv + 2.0 ** -14 * (ok @ np.abs(vd[b, h])) + \
                 2.0 ** -8 * np.abs(o) + 1e-5
             og = o_gpu[b, h, r]
             worst = max(worst, float(np.max(np.abs(og - o) / bound)))
             num += float(np.sum((og - o) ** 2))
             den += float(np.sum(o ** 2))
-            lerr = max(lerr, float(np.max(np.abs(lse_gpu[b, h, r] - lse))))
+            with np.errstate(invalid="ignore"):
+                dl = np.abs(lse_gpu[b, h, r] - lse)
+            dl = np.where(np.isneginf(lse) & np.isneginf(lse_gpu[b, h, r]), 0.0, dl)
+            lerr = max(lerr, float(np.max(dl / (1e-3 + delta))))
     return worst, math.sqrt(num / den), lerr
 
 
@@ -154,9 +172,9 @@ def test_forward_fp8_parity(gpu, name, shape, causal, rotate, padded):
     qd, kd, vd = O.dequantize_blocks(q8, sq), O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
     worst, rel, lerr = _check_forward(of, lg, qd, kd, vd, w.scale, causal, kv)
     print(f"{name} {shp} causal={causal} rotate={rotate} padded={padded}: "
-          f"max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  LSE {lerr:.2e}", flush=True)
+          f"max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  |dLSE|/bound {lerr:.3f}", flush=True)
     assert worst <= 1.0 and rel <= 5e-2
-    assert lerr <= 1e-3
+    assert lerr <= 1.0
     assert np.all(np.isfinite(of))
 
 
@@ -202,9 +220,9 @@ def test_forward_fp8_full_size_sampled_rows(gpu, causal):
     qd = O.dequantize_blocks(q8, sq)
     kd, vd = O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
     worst, rel, lerr = _check_forward(of, lg, qd, kd, vd, w.scale, causal, None, rows=rows)
-    print(f"full size causal={causal}: max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  LSE {lerr:.2e}",
+    print(f"full size causal={causal}: max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  |dLSE|/bound {lerr:.3f}",
           flush=True)
-    assert worst <= 1.0 and rel <= 5e-2 and lerr <= 1e-3
+    assert worst <= 1.0 and rel <= 5e-2 and lerr <= 1.0
 
 
 def test_forward_fp8_deterministic(gpu):
@@ -234,8 +252,8 @@ def test_forward_fp8_long_context_sampled_rows(gpu):
     qd = O.dequantize_blocks(q8, sq)
     kd, vd = O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
     worst, rel, lerr = _check_forward(of, lg, qd, kd, vd, w.scale, True, None, rows=rows)
-    print(f"long context: max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  LSE {lerr:.2e}", flush=True)
-    assert worst <= 1.0 and rel <= 5e-2 and lerr <= 1e-3
+    print(f"long context: max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  |dLSE|/bound {lerr:.3f}", flush=True)
+    assert worst <= 1.0 and rel <= 5e-2 and lerr <= 1.0
 
 
 @pytest.mark.parametrize("N", [1, 17, 64, 65])
@@ -253,7 +271,7 @@ def test_forward_fp8_edge_sizes(gpu, N, d, causal):
     of, lg = _run_forward(gpu, g, shp, w.scale, causal)
     qd, kd, vd = O.dequantize_blocks(q8, sq), O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
     worst, rel, lerr = _check_forward(of, lg, qd, kd, vd, w.scale, causal, None)
-    assert worst <= 1.0 and lerr <= 1e-3
+    assert worst <= 1.0 and lerr <= 1.0
     if N == 1:  # one key: O is that key's value row exactly up to bf16 rounding of O
         assert np.allclose(of[0, :, 0], vd[0, :, 0], rtol=2.0 ** -8, atol=1e-6)
 
@@ -271,7 +289,7 @@ def test_forward_fp8_empty_key_range(gpu):
     assert not of[0].any() and np.all(lg[0] == -np.inf)
     qd, kd, vd = O.dequantize_blocks(q8, sq), O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
     worst, rel, lerr = _check_forward(of[1:], lg[1:], qd[1:], kd[1:], vd[1:], w.scale, False, kv[1:])
-    assert worst <= 1.0 and lerr <= 1e-3
+    assert worst <= 1.0 and lerr <= 1.0
 
 
 def _bf16_tensor(gpu, x):
@@ -335,5 +353,5 @@ def test_forward_fp8_any_finite_scale(gpu, scale):
     of, lg = _run_forward(gpu, g, shp, scale, True)
     qd, kd, vd = O.dequantize_blocks(q8, sq), O.dequantize_blocks(k8, sk), O.dequantize_columns(v8, sv)
     worst, rel, lerr = _check_forward(of, lg, qd, kd, vd, scale, True, None)
-    print(f"fp8 scale {scale}: max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  LSE {lerr:.2e}", flush=True)
-    assert worst <= 1.0 and rel <= 5e-2 and lerr <= 1e-3
+    print(f"fp8 scale {scale}: max |dO|/bound {worst:.3f}  O rel-Frobenius {rel:.3e}  |dLSE|/bound {lerr:.3f}", flush=True)
+    assert worst <= 1.0 and rel <= 5e-2 and lerr <= 1.0

@@ -162,3 +162,60 @@ def test_coexec_values(gpu, micro, mode, valu_kind):
         np.testing.assert_allclose(got[:, 256:], np.tile(x.sum(axis=0), (blocks, 1)), rtol=2e-5, atol=0)
     else:
         np.testing.assert_array_equal(got[:, 256:], np.float32(0))
+
+
+def _fp8_tile(gpu, micro, a8, b8, c0):
+    import torch
+
+    micro.fa_micro_mfma_fp8_tile.argtypes = [ctypes.c_void_p] * 5
+    micro.fa_micro_mfma_fp8_tile.restype = ctypes.c_int
+    ta = torch.from_numpy(np.ascontiguousarray(a8, dtype=np.uint8)).to(gpu)
+    tb = torch.from_numpy(np.ascontiguousarray(b8, dtype=np.uint8)).to(gpu)
+    tc0 = torch.from_numpy(np.ascontiguousarray(c0, dtype=np.float32)).to(gpu)
+    tc = torch.full((32, 32), np.nan, dtype=torch.float32, device=gpu)
+    assert micro.fa_micro_mfma_fp8_tile(ta.data_ptr(), tb.data_ptr(), tc0.data_ptr(), tc.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    return tc.cpu().numpy().astype(np.float64)
+
+
+def _finite_codes(rng, shape, lo=0x00, hi=0x7E):
+    """Random E4M3 codes with magnitude codes in [lo, hi] (0x7F, NaN, excluded), random sign."""
+    mag = rng.integers(lo, hi, size=shape, endpoint=True).astype(np.uint8)
+    return mag | (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+
+
+def test_mfma_fp8_accumulation_precision(gpu, micro):
+    """Exact products and sums of the fp8 product on a wide spread of magnitudes: one
+    dominant product (448 x 448) per output beside 63 small ones, random codes, and a
+    large accumulator start; reports the error relative to the largest |product| of each
+    output.  Measured: at most 2^-11.8 of it (fp32 summation would stay within about
+    2^-18); the FP8 forward's parity bound takes 2^-10, which this asserts."""
+    from oracle import fp8 as O
+
+    P.say("micro mfma fp8 precision")
+    rng = np.random.default_rng(515)
+    cases = {}
+    a8, b8 = _finite_codes(rng, (32, 64)), _finite_codes(rng, (32, 64))
+    cases["random"] = (a8, b8, np.zeros((32, 32)))
+    a8, b8 = _finite_codes(rng, (32, 64), 0x08, 0x50), _finite_codes(rng, (32, 64), 0x08, 0x50)
+    a8[:, 0], b8[:, 0] = 0x7E, 0x7E
+    cases["dominant"] = (a8, b8, np.zeros((32, 32)))
+    a8, b8 = _finite_codes(rng, (32, 64), 0x08, 0x50), _finite_codes(rng, (32, 64), 0x08, 0x50)
+    a8[:, 0], b8[:, 0] = 0x7E, 0x7E
+    a8[:, 1], b8[:, 1] = 0x7E, 0xFE  # +448^2 - 448^2: the small products are the exact sum
+    cases["cancel"] = (a8, b8, np.zeros((32, 32)))
+    a8, b8 = _finite_codes(rng, (32, 64), 0x08, 0x50), _finite_codes(rng, (32, 64), 0x08, 0x50)
+    cases["big_start"] = (a8, b8, np.full((32, 32), 2.0**17))
+    for name, (a8, b8, c0) in cases.items():
+        a, b = O.e4m3_decode(a8), O.e4m3_decode(b8)
+        exact = a @ b.T + c0
+        got = _fp8_tile(gpu, micro, a8, b8, c0)
+        big = np.maximum(np.max(np.abs(a[:, None, :] * b[None, :, :]), axis=2), np.abs(c0))
+        err = np.abs(got - exact)
+        rel = err / big
+        small = exact - np.where(np.abs(c0) > 0, c0, 0.0)
+        P.say(f"  {name}: max |err| {err.max():.3e}, max |err|/max|term| {rel.max():.3e} "
+              f"(2^{np.log2(max(rel.max(), 1e-300)):.1f}), exact outputs {np.mean(err == 0):.2f}, "
+              f"mean signed err/|small| {np.mean((got - exact) / np.maximum(np.abs(small), 1e-30)):.3e}")
+        assert np.all(np.isfinite(got))
+        assert rel.max() <= 2.0**-10, name
