@@ -345,26 +345,36 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
 // ---------------------------------------------------------------------------------
 // Small-grid forward: 4 waves (one per SIMD) = 128 query rows per workgroup, two
 // workgroups per CU, a straight tile loop (copy tile j+1 | S_j, softmax, P V_j | store
-// V_{j+1}^T | barrier).  Each wave computes exactly what it computes in the kernel above
-// (same rows, tiles, order and arithmetic: outputs equal bit for bit, checked); the
+// V_{j+1}^T | barrier).  With G = 1 each wave computes exactly what it computes in the
+// kernel above (same rows, tiles, order and arithmetic: outputs equal bit for bit,
+// tested); the
 // smaller workgroups fill the GPU better where the 8-wave grid is small.  Measured on one
 // box (ms, 8-wave -> this kernel): BERT-shaped (8,16,512,64, padded) 0.0173 -> 0.0158,
 // GPT-2-shaped causal (8,12,1024,64) 0.0331 -> 0.0288, (1,2,128,64) 0.0070 -> 0.0053;
 // slower on large grids (d=128, N=8192: 1.06 -> 1.18; d=64, N=65536 causal: 9.86 ->
 // 10.44) and at d=128, N=2048 (0.0725 -> 0.0815).
 // ---------------------------------------------------------------------------------
-constexpr int kW2 = 4;                    // waves per workgroup (one per SIMD)
+constexpr int kW2 = 4;                    // waves per wave group (one per SIMD)
 constexpr int kBM2 = kW2 * kRowsPerWave;  // query rows per workgroup
-template <int D, int BN, bool CAUSAL, bool KVLEN>
-__global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
+// G = 1: one wave group, the whole key range.  G = 2 (split): two wave groups (8 waves,
+// two per SIMD) on the same 128 query rows, group g taking the g-th half of the key
+// tiles through LDS tiles of its own; the halves' (max, sum, O) are merged through LDS
+// at the end (so its sums differ from the unsplit kernels' in rounding only).  The split
+// halves every workgroup's tile count, so small grids (and the uneven blocks of a causal
+// mask) spread over twice as many SIMD slots.
+template <int D, int BN, bool CAUSAL, bool KVLEN, int G>
+__global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int TILE_BYTES = BN * D * 2;
   constexpr int NKB = BN / 32, NDB = D / 32, NKK = D / 16;
-  auto kbuf = [&](int i) { return smem + i * TILE_BYTES; };
-  auto vbuf = [&](int i) { return smem + (2 + i) * TILE_BYTES; };
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
+  const int wg = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
+  const int grp = G == 1 ? 0 : (wg >> 2), w = G == 1 ? wg : (wg & 3);
+  const int gtid = G == 1 ? tid : (tid & 255);
+  unsigned char* const gsm = smem + (size_t)grp * kLdsTiles * TILE_BYTES;
+  auto kbuf = [&](int i) { return gsm + i * TILE_BYTES; };
+  auto vbuf = [&](int i) { return gsm + (2 + i) * TILE_BYTES; };
   const int BH = p.B * p.H;
   const int nqb = (p.N + kBM2 - 1) / kBM2;
   int blk, bh;
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
   if constexpr (CAUSAL) wave_kend = min(kend, q0 + w * kRowsPerWave + kRowsPerWave);
 
   if (ntiles == 0) {
-    if (qrow < N) {
+    if ((G == 1 || grp == 0) && qrow < N) {
       f32x16 zero[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) zero[db] = f32x16{};
@@ -418,31 +428,37 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
   const float sl = p.scale_log2;
 
   VtHalf<BN, D> vh[2];
-  vh[0].init(tid, 0);
-  vh[1].init(tid, 1);
+  vh[0].init(gtid, 0);
+  vh[1].init(gtid, 1);
   const uint32_t kfrag = NatFrag<D>::base(c, h);
   const uint32_t vfrag[2] = {TrFrag<BN>::base(c, h, 0), TrFrag<BN>::base(c, h, 1)};
 
-  load_nat_tile<BN, D, kW2>(kg, 0, kv_end, kbuf(0), w, l);
-  vh[0].fetch(vg, 0, kv_end);
-  vh[1].fetch(vg, 0, kv_end);
+  // this group's tiles [jb, je); with G = 2 both groups run the first group's count of
+  // iterations (the second group's last one is empty when the count is odd)
+  const int half = G == 1 ? ntiles : (ntiles + 1) / 2;
+  const int jb = G == 1 ? 0 : grp * half, je = G == 1 ? ntiles : min(ntiles, jb + half);
+  if (G == 1 || jb < je) {
+    load_nat_tile<BN, D, kW2>(kg, jb * BN, kv_end, kbuf(0), w, l);
+    vh[0].fetch(vg, jb * BN, kv_end);
+    vh[1].fetch(vg, jb * BN, kv_end);
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    vh[0].store(vbuf(0), c4);
-    vh[1].store(vbuf(0), c4);
+    for (int c4 = 0; c4 < 4; ++c4) {
+      vh[0].store(vbuf(0), c4);
+      vh[1].store(vbuf(0), c4);
+    }
   }
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const bool nxt = j + 1 < ntiles;
+  for (int j = jb; j < jb + half; ++j) {
+    const bool nxt = j + 1 < je;
     if (nxt) {
-      load_nat_tile<BN, D, kW2>(kg, (j + 1) * BN, kv_end, kbuf((j + 1) & 1), w, l);
+      load_nat_tile<BN, D, kW2>(kg, (j + 1) * BN, kv_end, kbuf((j + 1 - jb) & 1), w, l);
       vh[0].fetch(vg, (j + 1) * BN, kv_end);
       vh[1].fetch(vg, (j + 1) * BN, kv_end);
     }
     const int kt0 = j * BN;
-    if (kt0 < wave_kend) {
-      const unsigned char* kt = kbuf(j & 1);
+    if ((G == 1 || j < je) && kt0 < wave_kend) {
+      const unsigned char* kt = kbuf((j - jb) & 1);
       f32x16 s[NKB];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
@@ -470,7 +486,7 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
       }
       u32x4 pk[NKB][2];
       softmax_tile<false, NKB, NDB>(s, sl, m_run, l_run, o, pk);
-      const unsigned char* vb_ = vbuf(j & 1);
+      const unsigned char* vb_ = vbuf((j - jb) & 1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -484,14 +500,39 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
     if (nxt) {
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        vh[0].store(vbuf((j + 1) & 1), c4);
-        vh[1].store(vbuf((j + 1) & 1), c4);
+        vh[0].store(vbuf((j + 1 - jb) & 1), c4);
+        vh[1].store(vbuf((j + 1 - jb) & 1), c4);
       }
     }
     wait_vmem();
     __syncthreads();
   }
 
+  if constexpr (G == 2) {
+    // merge: group 1 leaves (m, l, O) of each lane in LDS (the tiles are free after the
+    // loop's last barrier); group 0 rescales both halves to the larger reference
+    float* xo = (float*)smem + (size_t)(w * 64 + l) * (16 * NDB + 2);
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[16 * db + r] = o[db][r];
+      xo[16 * NDB] = m_run;
+      xo[16 * NDB + 1] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xo[16 * NDB], l1 = xo[16 * NDB + 1];
+    const float mm = fmaxf(m_run, m1);
+    const float mr = (mm == -INFINITY) ? 0.f : mm;
+    const float a0 = fast_exp2(m_run - mr), a1 = fast_exp2(m1 - mr);
+    m_run = mm;
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[16 * db + r] * a1;
+  }
   const float l_tot = half_sum(l_run);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
@@ -502,7 +543,10 @@ __global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
 }
 
 // Grids of the 8-wave kernel below this many workgroups (two per CU) run the small-grid
-// kernel when d = 64 (where it measured faster; at d = 128 it did not).
+// kernel when d = 64 (where it measured faster; at d = 128 it did not).  At d = 128 the
+// smallest grids run its split form instead (split_small_grid: B=1, H=16, N=2048 causal
+// 0.0598 -> 0.0476 ms, no mask 0.0624 -> 0.0519; B=2, H=16, N=2048 causal 0.0660 ->
+// 0.0628; one box), which measured slower at d = 64 and on fuller grids.
 constexpr unsigned kSmallGrid = 512;
 
 template <int D, int BN, bool CAUSAL, bool KVLEN>
@@ -510,8 +554,19 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   constexpr size_t lds = kLdsTiles * BN * D * 2;
   const unsigned bh = (unsigned)(a.B * a.H);
   const unsigned grid8 = (unsigned)((a.N + kBM - 1) / kBM) * bh;
+  if constexpr (D == 128) {
+    if (split_small_grid(grid8, CAUSAL)) {
+      auto kern = fa_fwd_small_kernel<D, BN, CAUSAL, KVLEN, 2>;
+      const size_t lds2 = 2 * lds;
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+      if (e != hipSuccess) return e;
+      const unsigned grid = (unsigned)((a.N + kBM2 - 1) / kBM2) * bh;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * kW2 * 64), lds2, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (D == 64 && grid8 < kSmallGrid) {
-    auto kern = fa_fwd_small_kernel<D, BN, CAUSAL, KVLEN>;
+    auto kern = fa_fwd_small_kernel<D, BN, CAUSAL, KVLEN, 1>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((a.N + kBM2 - 1) / kBM2) * bh;

@@ -100,6 +100,21 @@ inline ScaleSign scale_sign(float scale, uint32_t sign_bits) {
 constexpr uint32_t kSignBitsBf16 = 0x80008000u;
 constexpr uint32_t kSignBitsE4m3 = 0x80808080u;
 
+// Small d = 128 grids: the forward and the dQ pass then run 128-row workgroups whose
+// two wave groups take the two halves of the key range (merged in LDS), instead of one
+// 256-row workgroup per CU.  `grid8` is the unsplit launch's workgroup count (256 query
+// rows each).  Taken where that grid leaves at least half of the CUs idle, or, with the
+// causal mask (whose row blocks differ in cost), where it is at most one workgroup per
+// CU; measured slower on fuller grids (the split kernels do the same work per tile with
+// more per-workgroup overhead and no ping-pong of the two wave groups).
+inline bool split_small_grid(unsigned grid8, bool causal) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0)
+    return false;
+  return 2 * grid8 <= (unsigned)cus || (causal && grid8 <= (unsigned)cus);
+}
+
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_forward_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 hipError_t launch_fp8_quantize_rows(const uint16_t* x, uint8_t* x8, float* scales, const float* signs,

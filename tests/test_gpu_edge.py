@@ -7,6 +7,8 @@
 * head dim 64 at grids of 512 or more 8-wave workgroups (the 8-wave forward; smaller
   d = 64 grids run the 4-wave small-grid forward), with and without padding and causal
   masks, and the two forward kernels bit for bit equal on the same heads;
+* head dim 128 in both grid forms of the forward and the dQ pass (full-size grids and
+  the split form of small grids) on the same heads;
 * any finite scale: zero (uniform weights over the admissible keys) and negative scales,
   forward and backward.
 """
@@ -149,6 +151,41 @@ def test_d64_forward_kernels_agree(gpu, causal):
     torch.cuda.synchronize()
     assert np.array_equal(_bits(o8[:, :63]), _bits(o4))
     assert torch.equal(l8[:, :63], l4)
+
+
+# d = 128 problems run in two forms by grid size (split_small_grid in the library, for a
+# device of 256 CUs): with B*H*ceil(N/256) above 256 the 8-wave forward and the 8-wave
+# dQ pass; with few heads the split forms (two wave groups on the two halves of each
+# 128-row block's key range, merged in LDS).  N = 900 gives 15 key tiles (8 + 7), 257 and
+# 129 a ragged last tile.
+D128_FORM_CASES = [(900, True, (300, 900), 40), (900, False, None, 40), (257, True, None, 80), (129, False, (1, 129), 150)]
+
+
+@pytest.mark.parametrize("N,causal,kvr,H", D128_FORM_CASES,
+                         ids=lambda c: str(c) if not isinstance(c, bool) else ("causal" if c else "full"))
+def test_d128_split_and_unsplit_forms(gpu, N, causal, kvr, H):
+    import torch
+
+    B, d = 2, 128
+    P.say(f"d=128 grid forms: B={B} H={H} / 4 N={N} causal={causal} kv_range={kvr}")
+    inp = P.custom_inputs(B, H, N, d, seed=9800 + N + int(causal), causal=causal, kv_range=kvr, with_do=True)
+    t = inp.to_torch(gpu)
+    scale = d ** -0.5
+    o_big, lse_big, g_big = _fwd_bwd(t, causal, scale, t["kv_len"])
+    ts = {n: (x[:, :4].contiguous() if n != "kv_len" and x is not None else x) for n, x in t.items()}
+    o_sm, lse_sm, g_sm = _fwd_bwd(ts, causal, scale, ts["kv_len"])
+    torch.cuda.synchronize()
+    forms = {"unsplit": (o_big, lse_big, g_big), "split": (o_sm, lse_sm, g_sm)}
+    for b, h in [(0, 0), (1, 3), (0, 2)]:
+        kl = None if inp.kv_len is None else int(inp.kv_len[b])
+        qh, kh, vh, doh = (inp.head64(n, b, h)[None, None] for n in ("q", "k", "v", "do"))
+        kvh = None if kl is None else np.array([kl])
+        o_ref, lse_ref = ref.attention_forward(qh, kh, vh, scale, causal=causal, kv_len=kvh)
+        g_ref = ref.attention_backward(qh, kh, vh, doh, scale, causal=causal, kv_len=kvh)
+        for form, (o, lse, grads) in forms.items():
+            P.check_forward(P.to_np_bf16(o[b, h])[None, None], lse[b, h].cpu().numpy().astype(np.float64)[None, None],
+                            o_ref, lse_ref, label=f"{form} b{b} h{h}")
+            P.check_grads([P.to_np_bf16(g[b, h]) for g in grads], [r[0, 0] for r in g_ref], label=f"{form} b{b} h{h}")
 
 
 SCALE_CASES = [(1, 2, 128, 64, False, None), (2, 2, 300, 128, True, (100, 300)), (2, 2, 777, 64, True, None)]
