@@ -20,6 +20,9 @@ Low-level calls with the C names (caller allocates every output):
                     kv_len=None, stream=None)
     fa_backward_gqa_workspace_size(B, H, H_kv, N, d)
         grouped K/V heads: k, v, dk, dv are [B, H_kv, N, d] with H_kv dividing H
+    fa_forward_offset(q, k, v, o, lse, scale, causal, q_offset, kv_len=None, stream=None)
+        q, o [B, H, Nq, d] against k, v [B, H, Nk, d]; query row i at key position
+        q_offset + i (one GPU's share of a query-split forward)
 
 FP8 forward (block quantisation + incoherent processing; OCP E4M3 codes as uint8):
     fa_fp8_quantize_qk(x, x8, scales, signs=None, post_scale=1.0, stream=None)
@@ -52,6 +55,7 @@ __all__ = [
     "fa_backward_noalloc",
     "NOALLOC_SCRATCH_BYTES",
     "fa_forward_gqa",
+    "fa_forward_offset",
     "fa_backward_gqa",
     "fa_backward_gqa_workspace_size",
     "fa_fp8_quantize_qk",
@@ -142,6 +146,27 @@ def _kv_shape(q, k):
     if hkv < 1 or H % hkv:
         raise ValueError(f"K/V heads ({hkv}) must divide query heads ({H})")
     return (B, hkv, N, d)
+
+
+def fa_forward_offset(q, k, v, o, lse, scale, causal, q_offset, kv_len=None, stream=None):
+    """C ``fa_forward_offset``: q, o [B, H, Nq, d]; k, v [B, H, Nk, d]; query row i sits at
+    key position q_offset + i.  Fills o and lse [B, H, Nq] in place."""
+    _check_qkv("q", q)
+    shape = tuple(q.shape)
+    B, H, Nq, d = shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, {H}, Nk, {d}]")
+    kv_shape = tuple(k.shape)
+    _check_qkv("k", k, kv_shape)
+    _check_qkv("v", v, kv_shape)
+    _check_qkv("o", o, shape)
+    _check_lse(lse, shape)
+    lib = _lib.load()
+    kvp = _kv_ptr(kv_len, B, q.device)
+    sp = _stream_ptr(stream, q.device)
+    st = lib.fa_forward_offset(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq,
+                               int(kv_shape[2]), d, float(scale), int(bool(causal)), int(q_offset), kvp, sp)
+    _lib.check(st, "fa_forward_offset")
 
 
 def fa_forward_gqa(q, k, v, o, lse, scale, causal, kv_len=None, stream=None):

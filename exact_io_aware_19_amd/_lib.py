@@ -35,6 +35,7 @@ EXPORTED = (
     "fa_backward_dkdv_pass",
     "fa_backward_noalloc",
     "fa_forward_gqa",
+    "fa_forward_offset",
     "fa_backward_gqa",
     "fa_backward_gqa_workspace_size",
     "fa_fp8_quantize_qk",
@@ -75,6 +76,8 @@ def load():
     lib.fa_backward_noalloc.restype = i
     lib.fa_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
     lib.fa_forward_gqa.restype = i
+    lib.fa_forward_offset.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp]
+    lib.fa_forward_offset.restype = i
     lib.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.fa_backward_gqa.restype = i
     lib.fa_backward_gqa_workspace_size.argtypes = [i, i, i, i, i]

@@ -63,11 +63,17 @@ int check_kv_heads(int H, int Hkv) { return (Hkv >= 1 && H % Hkv == 0) ? FA_OK :
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Nk < 0: the square problem (Nk = N, query offset 0)
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
-                 int d, float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
+                 int d, float scale, int causal, const int32_t* kv_len, fa_stream_t stream, int Nk = -1,
+                 int q_off = 0) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
+  if (Nk < 0) Nk = N;
+  st = check_shape(B, H, Nk, d);
+  if (st != FA_OK) return st;
+  if (q_off < 0) return FA_ERR_SHAPE;
   st = check_kv_heads(H, Hkv);
   if (st != FA_OK) return st;
   st = check_scale(scale);
@@ -84,6 +90,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   a.H = H;
   a.Hkv = Hkv;
   a.N = N;
+  a.Nk = Nk;
+  a.q_off = q_off;
   a.d = d;
   const fa355::ScaleSign sg = fa355::scale_sign(scale, fa355::kSignBitsBf16);
   a.scale_log2 = sg.scale_log2;
@@ -167,6 +175,14 @@ int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float
 int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
                    int d, float scale, int causal, const int32_t* kv_len, fa_stream_t stream) {
   return forward_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, kv_len, stream);
+}
+
+int fa_forward_offset(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                      int Nk, int d, float scale, int causal, int q_offset, const int32_t* kv_len,
+                      fa_stream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (Nk < 1) return FA_ERR_SHAPE;  // (a negative Nk means the square problem internally)
+  return forward_impl(q, k, v, o, lse, B, H, H, Nq, d, scale, causal, kv_len, stream, Nk, q_offset);
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {

@@ -124,24 +124,26 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   block_order<!CAUSAL>((int)blockIdx.x, nqb, BH, blk, bh);
   const int qbi = CAUSAL ? (nqb - 1 - blk) : blk;
   const int b = bh / p.H;
-  const int N = p.N;
+  const int N = p.N, Nk = p.Nk;
   const size_t head = (size_t)bh * N * D;
   // grouped K/V heads: the H / Hkv query heads of a group share one K/V head
-  const size_t kv_head = (size_t)(b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * N * D;
+  const size_t kv_head = (size_t)(b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * Nk * D;
   const uint16_t* __restrict__ qg = p.q + head;
-  const buf_rsrc kg = make_rsrc(p.k + kv_head, (uint32_t)N * D * 2);
-  const buf_rsrc vg = make_rsrc(p.v + kv_head, (uint32_t)N * D * 2);
+  const buf_rsrc kg = make_rsrc(p.k + kv_head, (uint32_t)Nk * D * 2);
+  const buf_rsrc vg = make_rsrc(p.v + kv_head, (uint32_t)Nk * D * 2);
 
-  int kv_end = N;
-  if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);
+  int kv_end = Nk;
+  if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), Nk);
   const int q0 = qbi * kBM;
   const int qrow = q0 + w * kRowsPerWave + c;  // this lane's query row
+  // causal positions: query row i sits at key position q_off + i
+  const int cq0 = q0 + p.q_off, cqrow = qrow + p.q_off;
   int kend = kv_end;
-  if constexpr (CAUSAL) kend = min(kend, q0 + kBM);
+  if constexpr (CAUSAL) kend = min(kend, cq0 + kBM);
   const int ntiles = (kend + BN - 1) / BN;
   // keys past wave_kend are masked for every row of this wave (tile skipping)
   int wave_kend = kend;
-  if constexpr (CAUSAL) wave_kend = min(kend, q0 + w * kRowsPerWave + kRowsPerWave);
+  if constexpr (CAUSAL) wave_kend = min(kend, cq0 + w * kRowsPerWave + kRowsPerWave);
 
   if (ntiles == 0) {  // no admissible key for any row of this block (kv_len == 0)
     if (qrow < N) {
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
     const int kt0 = j * BN;
     if (j >= ntiles || kt0 >= wave_kend) return;
     bool need_mask = kt0 + BN > kv_end;
-    if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > q0 + w * kRowsPerWave);
+    if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > cq0 + w * kRowsPerWave);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
         for (int r = 0; r < 16; ++r) {
           const int key = kt0 + 32 * kb + c_row(r, h);
           bool bad = key >= kv_end;
-          if constexpr (CAUSAL) bad = bad || key > qrow;
+          if constexpr (CAUSAL) bad = bad || key > cqrow;
           s[kb][r] = bad ? -INFINITY : s[kb][r];
         }
     }
@@ -381,22 +383,23 @@ __global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdAr
   block_order<!CAUSAL>((int)blockIdx.x, nqb, BH, blk, bh);
   const int qbi = CAUSAL ? (nqb - 1 - blk) : blk;
   const int b = bh / p.H;
-  const int N = p.N;
+  const int N = p.N, Nk = p.Nk;
   const size_t head = (size_t)bh * N * D;
-  const size_t kv_head = (size_t)(b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * N * D;
+  const size_t kv_head = (size_t)(b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * Nk * D;
   const uint16_t* __restrict__ qg = p.q + head;
-  const buf_rsrc kg = make_rsrc(p.k + kv_head, (uint32_t)N * D * 2);
-  const buf_rsrc vg = make_rsrc(p.v + kv_head, (uint32_t)N * D * 2);
+  const buf_rsrc kg = make_rsrc(p.k + kv_head, (uint32_t)Nk * D * 2);
+  const buf_rsrc vg = make_rsrc(p.v + kv_head, (uint32_t)Nk * D * 2);
 
-  int kv_end = N;
-  if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), N);
+  int kv_end = Nk;
+  if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), Nk);
   const int q0 = qbi * kBM2;
   const int qrow = q0 + w * kRowsPerWave + c;
+  const int cq0 = q0 + p.q_off, cqrow = qrow + p.q_off;  // causal positions
   int kend = kv_end;
-  if constexpr (CAUSAL) kend = min(kend, q0 + kBM2);
+  if constexpr (CAUSAL) kend = min(kend, cq0 + kBM2);
   const int ntiles = (kend + BN - 1) / BN;
   int wave_kend = kend;
-  if constexpr (CAUSAL) wave_kend = min(kend, q0 + w * kRowsPerWave + kRowsPerWave);
+  if constexpr (CAUSAL) wave_kend = min(kend, cq0 + w * kRowsPerWave + kRowsPerWave);
 
   if (ntiles == 0) {
     if ((G == 1 || grp == 0) && qrow < N) {
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdAr
           s[kb] = mfma32(a, qf[kk], kk == 0 ? f32x16{} : s[kb]);
         }
       bool need_mask = kt0 + BN > kv_end;
-      if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > q0 + w * kRowsPerWave);
+      if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > cq0 + w * kRowsPerWave);
       if (need_mask) {
         // the limit is opaque here: otherwise the compiler sees that no key is past it
         // on tiles that need no mask and runs the selects on every tile
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdAr
           for (int r = 0; r < 16; ++r) {
             const int key = kt0 + 32 * kb + c_row(r, h);
             bool bad = key >= lim;
-            if constexpr (CAUSAL) bad = bad || key > qrow;
+            if constexpr (CAUSAL) bad = bad || key > cqrow;
             s[kb][r] = bad ? -INFINITY : s[kb][r];
           }
       }

@@ -12,7 +12,10 @@ struct FwdArgs {
   uint16_t* o;
   float* lse;
   const int32_t* kv_len;  // device int32[B] or nullptr
-  int B, H, N, d;
+  int B, H, N, d;    // N: query rows per head (of q, o, lse)
+  int Nk;            // key rows per head (of k, v); N for the square problem
+  int q_off;         // position of query row 0 in the key sequence (causal: key j is
+                     // admissible for query row i iff j <= q_off + i); 0 for the square problem
   int Hkv;           // K/V heads; query head h reads K/V head h / (H / Hkv)
   float scale_log2;  // |scale| * log2(e) (log2(e) when scale = 0)
   int causal;

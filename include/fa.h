@@ -78,6 +78,21 @@ int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float
                      float scale, int causal, const int32_t* kv_len, fa_stream_t stream);
 
 /*
+ * Forward pass for a block of Nq queries against Nk keys: query row i of q sits at
+ * position q_offset + i of the key sequence.  q, o: [B][H][Nq][d]; k, v: [B][H][Nk][d];
+ * lse: [B][H][Nq].  causal != 0: key j is admissible for query row i iff
+ * j <= q_offset + i; kv_len (device int32[B] or NULL) as in fa_forward_kvlen, clamped to
+ * [0, Nk].  With Nq = Nk and q_offset = 0 it is fa_forward_kvlen.  This is one GPU's share
+ * of a forward whose query rows are split over several GPUs that each hold all keys and
+ * values (or their admissible prefix): rows [q_offset, q_offset + Nq) of the whole
+ * problem's O and LSE, from the same definition ("FlashAttention" wiki page, 定義 (1)).
+ * Errors: as fa_forward; FA_ERR_SHAPE also for Nk < 1 or q_offset < 0.
+ */
+int fa_forward_offset(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                      int Nk, int d, float scale, int causal, int q_offset, const int32_t* kv_len,
+                      fa_stream_t stream);
+
+/*
  * Size in bytes of the device workspace fa_backward needs: two fp32 per query row,
  * -D_i (D_i = sum_k dO_ik O_ik) and LSE_i * log2(e), for N rounded up to a multiple of 256
  * rows per head: 8 * B * H * (256 * ceil(N / 256)) bytes.  dQ needs no accumulator: it

@@ -126,6 +126,24 @@ def test_backward_passes_validate_like_backward(lib, name):
     assert call(ws=FAKE + 16) == -7
 
 
+def _fwd_off(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=16, Nk=40, d=64, scale=0.125, causal=1,
+             q_offset=24):
+    return lib.fa_forward_offset(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, q_offset, None, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), -1), (dict(k=None), -1), (dict(lse=None), -1),
+        (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(Nk=-1), -2), (dict(q_offset=-1), -2), (dict(B=0), -2),
+        (dict(Nk=1 << 26, d=128), -2),
+        (dict(d=32), -3), (dict(scale=float("nan")), -4), (dict(v=FAKE + 4), -7), (dict(lse=FAKE + 1), -7),
+    ],
+)
+def test_forward_offset_rejects_invalid_arguments(lib, kw, status):
+    assert _fwd_off(lib, **kw) == status
+
+
 @pytest.mark.parametrize("H,Hkv,status", [(4, 3, -8), (4, 0, -8), (4, -2, -8), (4, 5, -8), (0, 1, -2)])
 def test_gqa_entry_points_reject_bad_kv_heads(lib, H, Hkv, status):
     assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, H, Hkv, 16, 64, 0.125, 0, None, None) == status
