@@ -506,6 +506,8 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
                     _alg_bytes(B, H, N, d, direction, w.kv_heads) / (cms * 1e-3) / 1e9, 1)
         if name in ("tiny", "bert_large", "gpt2"):
             res["step"] = time_step_graph(lib, torch, dev, t, w)
+        if name == "long_64k":
+            res["query_shards"] = time_query_shards(lib, torch, stream, t, w)
         if name.startswith("sweep_n") or name == "long_64k":
             # the FP8 forward on the same inputs (block quantisation + incoherent processing)
             res["fwd_fp8"] = {k: v for k, v in run_fp8(fa, wl, torch, dev, stream, t, w, iters)[
@@ -514,6 +516,47 @@ def run_sweep(fa, wl, torch, dev, stream, iters=10):
         out.append(res)
         del t, o, lse
         torch.cuda.empty_cache()
+    return out
+
+
+def time_query_shards(lib, torch, stream, t, w, gpus=8, iters=5):
+    """One GPU's share of the causal forward split by query rows over `gpus` GPUs that each
+    hold all keys and values (fa_forward_offset; the all-gather of K and V is not part of
+    it): contiguous shares of N/gpus rows, and the zig-zag assignment (2*gpus pieces, GPU g
+    takes pieces g and 2*gpus-1-g, which balances the causal work).  Returns each GPU's
+    time, the slowest one, and the whole problem's FLOPs over that time (the rate the
+    GPUs would reach together if the exchange hides behind the compute)."""
+    B, H, N, d = w.shape
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=t["q"].device)
+    sp = stream.cuda_stream
+
+    def piece_ms(r0, r1):
+        q = t["q"][:, :, r0:r1].contiguous()
+        args = (q.data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, r1 - r0, N,
+                d, w.scale, int(w.causal), r0, None, sp)
+        st = lib.fa_forward_offset(*args)
+        if st != 0:
+            raise RuntimeError(f"fa_forward_offset returned {st}")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            lib.fa_forward_offset(*args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    n = N // gpus
+    contiguous = [piece_ms(g * n, (g + 1) * n) for g in range(gpus)]
+    h = n // 2
+    pieces = [piece_ms(p * h, (p + 1) * h) for p in range(2 * gpus)]
+    zigzag = [pieces[g] + pieces[2 * gpus - 1 - g] for g in range(gpus)]
+    out = {"gpus": gpus, "rows_per_gpu": n}
+    for name, per in (("contiguous", contiguous), ("zigzag", zigzag)):
+        worst = max(per)
+        out[name] = {"per_gpu_ms": [round(x, 4) for x in per], "max_ms": round(worst, 4),
+                     "tflops_all_gpus": round(w.fwd_flops() / (worst * 1e-3) / 1e12, 1)}
     return out
 
 
