@@ -73,7 +73,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (Nk < 0) Nk = N;
   st = check_shape(B, H, Nk, d);
   if (st != FA_OK) return st;
-  if (q_off < 0) return FA_ERR_SHAPE;
+  // causal positions q_off + row (+ a block) stay in int range
+  if (q_off < 0 || (long long)q_off + N + 256 > 0x7fffffffLL) return FA_ERR_SHAPE;
   st = check_kv_heads(H, Hkv);
   if (st != FA_OK) return st;
   st = check_scale(scale);

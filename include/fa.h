@@ -86,7 +86,8 @@ int fa_forward_kvlen(const void* q, const void* k, const void* v, void* o, float
  * of a forward whose query rows are split over several GPUs that each hold all keys and
  * values (or their admissible prefix): rows [q_offset, q_offset + Nq) of the whole
  * problem's O and LSE, from the same definition ("FlashAttention" wiki page, 定義 (1)).
- * Errors: as fa_forward; FA_ERR_SHAPE also for Nk < 1 or q_offset < 0.
+ * Errors: as fa_forward; FA_ERR_SHAPE also for Nk < 1, q_offset < 0 or
+ * q_offset + Nq + 256 > 2^31 - 1.
  */
 int fa_forward_offset(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
                       int Nk, int d, float scale, int causal, int q_offset, const int32_t* kv_len,

@@ -136,6 +136,7 @@ def _fwd_off(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=16, Nk=
     [
         (dict(q=None), -1), (dict(k=None), -1), (dict(lse=None), -1),
         (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(Nk=-1), -2), (dict(q_offset=-1), -2), (dict(B=0), -2),
+        (dict(q_offset=(1 << 31) - 200), -2),
         (dict(Nk=1 << 26, d=128), -2),
         (dict(d=32), -3), (dict(scale=float("nan")), -4), (dict(v=FAKE + 4), -7), (dict(lse=FAKE + 1), -7),
     ],
