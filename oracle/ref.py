@@ -54,6 +54,7 @@ __all__ = [
     "attention_backward",
     "forward_rows",
     "backward_dq_rows",
+    "backward_dkdv_cols",
 ]
 
 _ROW_CHUNK = 1024
@@ -214,3 +215,29 @@ def backward_dq_rows(q, k, v, do, scale, rows, causal=False, kv_len_b=None):
     dsum = (p * dp).sum(axis=1)
     ds = p * (dp - dsum[:, None])
     return scale * (ds @ k)
+
+
+def backward_dkdv_cols(q, k, v, do, scale, cols, causal=False, kv_len_b=None):
+    """dK and dV of a few key rows ("columns" of P) of ONE head.  Key j's gradients sum
+    over every query row: dV_j = sum_i P_ij dO_i and dK_j = scale * sum_i dS_ij Q_i with
+    dS_ij = P_ij (dP_ij - D_i).  Each P row is normalised over all of its keys and each
+    D_i sums over all of its keys, so every query row is still computed in full (in row
+    chunks, as attention_backward does); only the selected columns are kept."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    cols = np.asarray(cols, dtype=np.int64)
+    n, d = q.shape
+    dk = np.zeros((cols.shape[0], d))
+    dv = np.zeros((cols.shape[0], d))
+    for r0 in range(0, n, _ROW_CHUNK):
+        rows = np.arange(r0, min(n, r0 + _ROW_CHUNK))
+        s = scale * (q[rows] @ k.T)
+        ok = admissible(rows, n, causal, kv_len_b)
+        p, _ = _softmax_rows(s, ok)
+        dor = do[rows]
+        dp = dor @ v.T
+        dsum = (p * dp).sum(axis=1)
+        p_c = p[:, cols]
+        ds_c = p_c * (dp[:, cols] - dsum[:, None])
+        dv += p_c.T @ dor
+        dk += scale * (ds_c.T @ q[rows])
+    return dk, dv

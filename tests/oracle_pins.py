@@ -324,6 +324,41 @@ def pin_sampled_rows_match_full(ref, online):
             np.testing.assert_allclose(dqr, dq[b, 0, rows], rtol=0, atol=1e-13)
 
 
+def pin_sampled_key_columns(ref, online):
+    """dK, dV of selected key rows (backward_dkdv_cols) against torch float64 autograd
+    and against the full oracle backward, whole-row and in chunks of 3 and 7 query rows,
+    every mask mode, a positive and a negative scale; the selection includes the first
+    and last key and, with padding, keys past kv_len (zero gradients)."""
+    import torch
+    import torch.nn.functional as F
+
+    saved = ref._ROW_CHUNK
+    try:
+        for seed, (N, d, scale) in enumerate([(21, 5, 0.55), (34, 6, -0.35)]):
+            for mode in MASK_MODES:
+                rng, q, k, v, do = _inputs(1470 + seed, 2, 1, N, d, with_do=True)
+                causal, kv = _mask_args(mode, rng, 2, N)
+                cols = np.array([N - 1, 0, 7, 3, N // 2, N - 2])
+                ref._ROW_CHUNK = saved
+                _, dk_full, dv_full = ref.attention_backward(q, k, v, do, scale, causal=causal, kv_len=kv)
+                for b in range(2):
+                    kl = None if kv is None else kv[b]
+                    m = _torch_mask(N, causal, kl)
+                    tq, tk, tv = (torch.from_numpy(x[b, 0].copy()).requires_grad_(True) for x in (q, k, v))
+                    to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale)
+                    to.backward(torch.from_numpy(do[b, 0]))
+                    for chunk in (saved, 3, 7):
+                        ref._ROW_CHUNK = chunk
+                        dkc, dvc = ref.backward_dkdv_cols(q[b, 0], k[b, 0], v[b, 0], do[b, 0], scale, cols,
+                                                          causal=causal, kv_len_b=None if kl is None else int(kl))
+                        np.testing.assert_allclose(dkc, tk.grad.numpy()[cols], rtol=0, atol=1e-11)
+                        np.testing.assert_allclose(dvc, tv.grad.numpy()[cols], rtol=0, atol=1e-11)
+                        np.testing.assert_allclose(dkc, dk_full[b, 0, cols], rtol=0, atol=1e-12)
+                        np.testing.assert_allclose(dvc, dv_full[b, 0, cols], rtol=0, atol=1e-12)
+    finally:
+        ref._ROW_CHUNK = saved
+
+
 def pin_row_chunks(ref, online):
     """The oracle's row-chunked path (taken for long sequences) against torch float64
     SDPA and autograd and against the single-chunk result, with chunks of 3 and 7 rows
@@ -454,6 +489,7 @@ ALL_PINS = [
     pin_permutation,
     pin_dk_columns_sum_to_zero,
     pin_sampled_rows_match_full,
+    pin_sampled_key_columns,
     pin_row_chunks,
     pin_online_equals_two_pass,
     pin_torch_sdpa_gqa,

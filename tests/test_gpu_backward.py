@@ -79,14 +79,15 @@ def test_backward_workload_full(gpu, name):
                                           ("sweep_n16384_causal", 1)])
 def test_backward_workload_sampled_heads(gpu, name, n_heads):
     """Full sizes in the launch configuration the bench times; the oracle computes the
-    complete gradients of a few seeded heads, plus dQ rows of more heads."""
+    complete gradients of a few seeded heads, plus dQ rows and dK, dV key rows of three
+    more heads."""
     w = wl.get_workload(name)
     P.say(f"backward workload {name} {w.shape} causal={w.causal} (sampled heads)")
     inp = wl.generate(w, with_do=True)
     _, _, _, grads = _run(inp, gpu)
     g_np = [P.to_np_bf16(g) for g in grads]
     rng = np.random.default_rng(w.seed + 29)
-    heads = [(int(rng.integers(0, w.B)), int(rng.integers(0, w.H))) for _ in range(n_heads + 3)]
+    heads = [divmod(int(x), w.H) for x in rng.choice(w.B * w.H, n_heads + 3, replace=False)]  # distinct
     for j, (b, h) in enumerate(heads):
         qh, kh, vh, doh = (inp.head64(n, b, h) for n in ("q", "k", "v", "do"))
         if j < n_heads:
@@ -97,8 +98,14 @@ def test_backward_workload_sampled_heads(gpu, name, n_heads):
             rows = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, 64, replace=False)]))
             dq_ref = ref.backward_dq_rows(qh, kh, vh, doh, w.scale, rows, causal=w.causal)
             err = P.rel_frob(g_np[0][b, h, rows], dq_ref)
-            P.say(f"  {name} b{b} h{h} dQ rows: rel-Frobenius {err:.3e}")
+            cols = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, 64, replace=False)]))
+            dk_ref, dv_ref = ref.backward_dkdv_cols(qh, kh, vh, doh, w.scale, cols, causal=w.causal)
+            err_k, err_v = P.rel_frob(g_np[1][b, h, cols], dk_ref), P.rel_frob(g_np[2][b, h, cols], dv_ref)
+            P.say(f"  {name} b{b} h{h} rel-Frobenius: dQ rows {err:.3e}, dK key rows {err_k:.3e}, "
+                  f"dV key rows {err_v:.3e}")
             assert err <= P.GRAD_REL
+            assert err_k <= P.GRAD_REL
+            assert err_v <= P.GRAD_REL
 
 
 def test_backward_deterministic(gpu):

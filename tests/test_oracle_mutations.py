@@ -36,6 +36,11 @@ REF_MUTATIONS = {
                               "rows = np.arange(0, min(N, _ROW_CHUNK))"),
     "chunk_last_rows_dropped": ("rows = np.arange(r0, min(n, r0 + _ROW_CHUNK))",
                                 "rows = np.arange(r0, min(n - 1, r0 + _ROW_CHUNK))"),
+    "cols_dv_p_not_transposed": ("dv += p_c.T @ dor", "dv += p_c @ dor"),
+    "cols_d_over_selected_keys_only": ("dsum = (p * dp).sum(axis=1)\n        p_c",
+                                       "dsum = (p[:, cols] * dp[:, cols]).sum(axis=1)\n        p_c"),
+    "cols_dk_chunk_overwrites": ("dk += scale * (ds_c.T @ q[rows])", "dk = scale * (ds_c.T @ q[rows])"),
+    "cols_dk_missing_scale": ("dk += scale * (ds_c.T @ q[rows])", "dk += (ds_c.T @ q[rows])"),
     "gqa_interleaved_heads": ("return attention_forward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)",
                               "return attention_forward(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1))"),
     "gqa_dk_not_summed": ("return dq, dk.reshape(B, Hkv, G, N, d).sum(axis=2)",
