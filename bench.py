@@ -118,6 +118,104 @@ def _quantile(xs, q):
     return ys[lo] + (ys[hi] - ys[lo]) * (pos - lo)
 
 
+def parse_current_sclk_mhz(text):
+    """Current gfx clock (MHz) from the text of the amdgpu sysfs file pp_dpm_sclk: the
+    line marked with '*' (a live reading such as 'S: 1843Mhz *', or a DPM level)."""
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*mhz", line, re.IGNORECASE)
+            if m:
+                return int(m.group(1))
+    return None
+
+
+def gpu_sysfs_dir(torch):
+    """sysfs device directory of GPU 0 (the card with pp_dpm_sclk; with several cards, the
+    one on GPU 0's PCI bus), or None."""
+    import glob
+
+    cards = sorted(os.path.dirname(f) for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if len(cards) <= 1:
+        return cards[0] if cards else None
+    bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+    for c in cards:
+        addr = os.path.basename(os.path.realpath(c))  # domain:bus:device.function
+        try:
+            if bus is not None and int(addr.split(":")[1], 16) == int(bus):
+                return c
+        except (IndexError, ValueError):
+            pass
+    return None
+
+
+class ClockSampler:
+    """Samples the gfx clock (pp_dpm_sclk) and the board power (hwmon power1_input) from
+    sysfs on a host thread: file reads only, no GPU calls (but each clock read queries the
+    power-management firmware, which perturbs the GPU, so never during timed work)."""
+
+    def __init__(self, devdir, period_s=0.005):
+        import glob
+        import threading
+
+        self.devdir, self.period = devdir, period_s
+        hw = sorted(glob.glob(os.path.join(devdir, "hwmon", "hwmon*"))) if devdir else []
+        self.power_in = os.path.join(hw[0], "power1_input") if hw else None
+        self.power_cap = os.path.join(hw[0], "power1_cap") if hw else None
+        self.sclk, self.power = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        with open(path) as f:
+            return f.read()
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                mhz = parse_current_sclk_mhz(self._read(os.path.join(self.devdir, "pp_dpm_sclk")))
+                if mhz is not None:
+                    self.sclk.append(mhz)
+                if self.power_in and os.path.exists(self.power_in):
+                    self.power.append(int(self._read(self.power_in)) / 1e6)
+            except (OSError, ValueError):
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.devdir:
+            self._thread.start()
+        return self
+
+    def stop(self):
+        """Summary of the samples (None without a readable clock)."""
+        if not self.devdir:
+            return None
+        self._stop.set()
+        self._thread.join(timeout=2.0)
+        if not self.sclk:
+            return None
+        cap = None
+        try:
+            if self.power_cap and os.path.exists(self.power_cap):
+                cap = round(int(self._read(self.power_cap)) / 1e6, 1)
+        except (OSError, ValueError):
+            pass
+        out = {
+            "source": "sysfs pp_dpm_sclk (current gfx clock) and hwmon power1_input, read every "
+                      f"{self.period * 1e3:.0f} ms on a host thread",
+            "samples": len(self.sclk),
+            "sclk_mhz_median": round(_quantile(self.sclk, 0.5), 1),
+            "sclk_mhz_min": min(self.sclk),
+            "sclk_mhz_max": max(self.sclk),
+            "power_cap_w": cap,
+        }
+        if self.power:
+            out["power_w_median"] = round(_quantile(self.power, 0.5), 1)
+            out["power_w_max"] = round(max(self.power), 1)
+        return out
+
+
 def bench_workload(n):
     """The large-head workload of the step: B=2, H=16, d=128, N=n, scale 1/sqrt(d), seeded
     like the sweep's (the same inputs for both mask modes)."""
@@ -175,6 +273,18 @@ def run_gpu(args):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # The gfx clock and board power, sampled while 20 more (untimed) steps of the same work
+    # run right after the timed ones, once they are all enqueued: reading the clock from
+    # sysfs queries the power-management firmware and, done during the timed steps,
+    # left the GPU idle between kernels (whole-step rate -17%, kernel times unchanged).
+    sampler = ClockSampler(gpu_sysfs_dir(torch))
+    for _ in range(20):
+        step(False)
+    sampler.start()
+    torch.cuda.synchronize()
+    clock = sampler.stop()
+    if clock:
+        clock["during"] = "20 untimed steps of the same work right after the timed steps"
 
     kms = {c: sum(a.elapsed_time(b) for a, b in ev[c]) / len(ev[c]) for c in kern_calls}
     per_step = {c: [a.elapsed_time(b) for a, b in ev[c]] for c in kern_calls}
@@ -209,6 +319,8 @@ def run_gpu(args):
     step_ms = [sum(per_step[c][i] for c in kern_calls) for i in range(args.steps)]
     detail["step_kernels_ms_median"] = round(_quantile(step_ms, 0.5), 4)
     detail["step_kernels_ms_max"] = round(max(step_ms), 4)
+    # the gfx clock this work runs at (the peak assumes 2.4 GHz)
+    detail["clock"] = clock
     # dominant kernel = the one with the largest share of the step time, by the median
     # launch (a single stalled launch must not make another kernel the dominant one)
     kmed = {c: _quantile(per_step[c], 0.5) for c in kern_calls}

@@ -1,7 +1,7 @@
 """CPU tests of the bench's host logic: the FLOP and byte conventions, the HBM-traffic
 summary built from rocprofv3 counter CSVs (calibration by the plain copies, per-kernel and
-per-grid rows), the staleness check of the committed traffic figure, and the refusal of
-more than one GPU."""
+per-grid rows), the staleness check of the committed traffic figure, the refusal of more
+than one GPU, and the clock/power sampler's parsing of sysfs."""
 
 import csv
 import os
@@ -126,3 +126,28 @@ def test_cpu_baseline_runs_a_spawned_single_threaded_pool():
     assert out["cores"] == bench.cpu_worker_count() <= 16
     assert "4 tasks" in out["sample"]
     assert out["full_step_seconds_extrapolated"] == round(out["seconds"] * 4 / 4, 1)
+
+
+def test_current_sclk_is_the_marked_line():
+    # a live reading (as MI355X reports it) and a marked DPM level
+    assert bench.parse_current_sclk_mhz("S: 1843Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 1843
+    assert bench.parse_current_sclk_mhz("0: 500Mhz\n1: 2100Mhz *\n2: 2400Mhz\n") == 2100
+    assert bench.parse_current_sclk_mhz("0: 500Mhz\n1: 2400Mhz\n") is None
+
+
+def test_clock_sampler_summarises_sysfs(tmp_path):
+    dev = tmp_path / "device"
+    (dev / "hwmon" / "hwmon3").mkdir(parents=True)
+    (dev / "pp_dpm_sclk").write_text("S: 1790Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    (dev / "hwmon" / "hwmon3" / "power1_input").write_text("1375000000\n")
+    (dev / "hwmon" / "hwmon3" / "power1_cap").write_text("1400000000\n")
+    s = bench.ClockSampler(str(dev), period_s=0.001).start()
+    import time
+
+    time.sleep(0.05)
+    out = s.stop()
+    assert out["samples"] >= 1
+    assert out["sclk_mhz_median"] == out["sclk_mhz_min"] == out["sclk_mhz_max"] == 1790
+    assert out["power_w_median"] == 1375.0 and out["power_cap_w"] == 1400.0
+    # no sysfs directory: no summary, and no thread started
+    assert bench.ClockSampler(None).start().stop() is None
