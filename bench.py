@@ -254,11 +254,15 @@ def run_gpu(args):
             fa.fa_backward_pass(kind, q, k, v, o[causal], do, lse[causal], dq, dk, dv, scale, causal, ws,
                                 stream=stream)
 
-    def step(record):
-        for c in kern_calls:
+    # every timing event exists before the timed region: creating events inside it put
+    # host work between an event and its kernel
+    pool = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in kern_calls]
+            for _ in range(args.steps)]
+
+    def step(record, i=0):
+        for j, c in enumerate(kern_calls):
             if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0, e1 = pool[i][j]
                 e0.record(stream)
             launch(*c)
             if record:
@@ -269,22 +273,26 @@ def run_gpu(args):
         step(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
+    for i in range(args.steps):
+        step(True, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # The gfx clock and board power, sampled while 20 more (untimed) steps of the same work
     # run right after the timed ones, once they are all enqueued: reading the clock from
     # sysfs queries the power-management firmware and, done during the timed steps,
     # left the GPU idle between kernels (whole-step rate -17%, kernel times unchanged).
-    sampler = ClockSampler(gpu_sysfs_dir(torch))
-    for _ in range(20):
-        step(False)
-    sampler.start()
-    torch.cuda.synchronize()
-    clock = sampler.stop()
-    if clock:
-        clock["during"] = "20 untimed steps of the same work right after the timed steps"
+    # Only runs that time at least 10 steps do this: the short runs the profiler commands
+    # make keep their launch counts and read no sysfs while counters are collected.
+    clock = None
+    if args.steps >= 10 and args.clock_steps > 0:
+        sampler = ClockSampler(gpu_sysfs_dir(torch))
+        for _ in range(args.clock_steps):
+            step(False)
+        sampler.start()
+        torch.cuda.synchronize()
+        clock = sampler.stop()
+        if clock:
+            clock["during"] = f"{args.clock_steps} untimed steps of the same work right after the timed steps"
 
     kms = {c: sum(a.elapsed_time(b) for a, b in ev[c]) / len(ev[c]) for c in kern_calls}
     per_step = {c: [a.elapsed_time(b) for a, b in ev[c]] for c in kern_calls}
@@ -906,6 +914,9 @@ def main(argv=None):
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the FP8 forward (timed after the bf16 step, reported under detail)")
     ap.add_argument("--fp8-iters", type=int, default=20, help="timed iterations of the FP8 forward (default 20)")
+    ap.add_argument("--clock-steps", type=int, default=20,
+                    help="untimed steps after the timed ones during which the gfx clock and board power are sampled "
+                         "(default 20; only when --steps >= 10; 0: none)")
     ap.add_argument("--no-machine", dest="machine", action="store_false",
                     help="skip the machine microbenchmarks (sustained MFMA, exp, LDS, atomic rates)")
     ap.add_argument("--copy-calibration", action="store_true",
