@@ -403,15 +403,16 @@ def run_fp8(fa, wl, torch, dev, stream, t, w, iters):
     for fn in calls.values():
         for _ in range(3):
             fn()
+    # the events exist before the timed calls (see run_gpu)
+    ev = {key: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+          for key in calls}
     torch.cuda.synchronize()
-    ev = {key: [] for key in calls}
-    for _ in range(iters):
+    for i in range(iters):
         for key, fn in calls.items():
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = ev[key][i]
             e0.record(stream)
             fn()
             e1.record(stream)
-            ev[key].append((e0, e1))
     torch.cuda.synchronize()
     ms = {key: sum(a.elapsed_time(b) for a, b in v) / len(v) for key, v in ev.items()}
     out = {}
