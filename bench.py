@@ -161,7 +161,14 @@ class ClockSampler:
         hw = sorted(glob.glob(os.path.join(devdir, "hwmon", "hwmon*"))) if devdir else []
         self.power_in = os.path.join(hw[0], "power1_input") if hw else None
         self.power_cap = os.path.join(hw[0], "power1_cap") if hw else None
-        self.sclk, self.power = [], []
+        self.temp_in = None  # the sensor labelled "junction"
+        for lab in sorted(glob.glob(os.path.join(hw[0], "temp*_label"))) if hw else []:
+            try:
+                if self._read(lab).strip() == "junction":
+                    self.temp_in = lab[: -len("_label")] + "_input"
+            except OSError:
+                pass
+        self.sclk, self.power, self.temp = [], [], []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -178,6 +185,8 @@ class ClockSampler:
                     self.sclk.append(mhz)
                 if self.power_in and os.path.exists(self.power_in):
                     self.power.append(int(self._read(self.power_in)) / 1e6)
+                if self.temp_in and os.path.exists(self.temp_in):
+                    self.temp.append(int(self._read(self.temp_in)) / 1e3)
             except (OSError, ValueError):
                 return
             self._stop.wait(self.period)
@@ -202,7 +211,7 @@ class ClockSampler:
         except (OSError, ValueError):
             pass
         out = {
-            "source": "sysfs pp_dpm_sclk (current gfx clock) and hwmon power1_input, read every "
+            "source": "sysfs pp_dpm_sclk (current gfx clock), hwmon power1_input and junction temperature, read every "
                       f"{self.period * 1e3:.0f} ms on a host thread",
             "samples": len(self.sclk),
             "sclk_mhz_median": round(_quantile(self.sclk, 0.5), 1),
@@ -213,6 +222,9 @@ class ClockSampler:
         if self.power:
             out["power_w_median"] = round(_quantile(self.power, 0.5), 1)
             out["power_w_max"] = round(max(self.power), 1)
+        if self.temp:
+            out["junction_c_median"] = round(_quantile(self.temp, 0.5), 1)
+            out["junction_c_max"] = round(max(self.temp), 1)
         return out
 
 

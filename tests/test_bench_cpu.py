@@ -141,6 +141,10 @@ def test_clock_sampler_summarises_sysfs(tmp_path):
     (dev / "pp_dpm_sclk").write_text("S: 1790Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
     (dev / "hwmon" / "hwmon3" / "power1_input").write_text("1375000000\n")
     (dev / "hwmon" / "hwmon3" / "power1_cap").write_text("1400000000\n")
+    (dev / "hwmon" / "hwmon3" / "temp2_label").write_text("junction\n")
+    (dev / "hwmon" / "hwmon3" / "temp2_input").write_text("81000\n")
+    (dev / "hwmon" / "hwmon3" / "temp3_label").write_text("mem\n")
+    (dev / "hwmon" / "hwmon3" / "temp3_input").write_text("60000\n")
     s = bench.ClockSampler(str(dev), period_s=0.001).start()
     import time
 
@@ -149,5 +153,6 @@ def test_clock_sampler_summarises_sysfs(tmp_path):
     assert out["samples"] >= 1
     assert out["sclk_mhz_median"] == out["sclk_mhz_min"] == out["sclk_mhz_max"] == 1790
     assert out["power_w_median"] == 1375.0 and out["power_cap_w"] == 1400.0
+    assert out["junction_c_median"] == out["junction_c_max"] == 81.0
     # no sysfs directory: no summary, and no thread started
     assert bench.ClockSampler(None).start().stop() is None
