@@ -536,6 +536,20 @@ def run_machine(torch, dev, stream, reps=3):
             ms[key] = round(sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2], 4)
         ms["overlap"] = round((ms["exp_ms"] + ms["fma_ms"] - ms["both_ms"]) / min(ms["exp_ms"], ms["fma_ms"]), 3)
         res[name] = ms
+    # shader-clock cycles per 32 products in the attention forward's order against 8
+    # independent chains (32 x 32 = 1024 at best), one wave per SIMD on every CU
+    lib.fa_micro_mfma_order.argtypes = [vp, vp, i, i, i, vp]
+    lib.fa_micro_mfma_order.restype = i
+    oblocks, oiters = blocks // 2, 2000
+    ticks = torch.zeros(oblocks * 4, dtype=torch.int64, device=dev)
+    order = {}
+    for variant, key in ((0, "independent_chains"), (1, "forward_order"), (2, "forward_order_scores_4_chains"),
+                         (3, "forward_order_lds_operands")):
+        if lib.fa_micro_mfma_order(ticks.data_ptr(), out.data_ptr(), oblocks, variant, oiters, sp) != 0:
+            raise RuntimeError(f"mfma order variant {variant}: launch failed")
+        torch.cuda.synchronize()
+        order[key] = round(float(ticks.double().median().item()) / oiters, 1)
+    res["mfma_order_cycles_per_32_products"] = order
     return res
 
 

@@ -1,6 +1,7 @@
 // Microbenchmarks of the gfx950 units the attention kernels are bound by: the bf16 MFMA
 // rate the chip sustains (its clock under load included), the v_exp_f32 rate, LDS read
-// bandwidth, fp32 global atomic throughput and MFMA/VALU co-execution on one SIMD.  They measure the machine, not attention:
+// bandwidth, fp32 global atomic throughput, MFMA/VALU co-execution on one SIMD and the issue
+// rate of the forward's product order.  They measure the machine, not attention:
 // the bench reports them beside the data-sheet peaks.  C ABI in include/fa_micro.h
 // (libfa355_micro.so, a library of its own).
 #include <hip/hip_runtime.h>
@@ -172,6 +173,118 @@ __global__ __launch_bounds__(kCoexThreads, 1) void coexec_loop(float* __restrict
   o[tid] = res;
 }
 
+// Issue rate of 32 bf16 products per block in a given order, one wave per SIMD (a
+// 256-thread workgroup per compute unit: 96 KiB of LDS keeps a second one off).  A
+// operands are bf16 2^-10 (in registers, or in LDS for variant 3); accumulation chain k
+// takes the B operand bf16 2^-10 (1 + k/128), so no two chains compute the same values
+// (identical chains were merged by the compiler: 829 ticks per 32 products, below the
+// 1024 the MFMA unit allows).  Lane 0 of each wave writes the s_memtime difference
+// (shader-clock ticks) over the `iters` blocks.
+//   0: 8 independent accumulation chains, 4 products each per block;
+//   1: the forward's MFMA operation -- 16 P.V products over 4 accumulators (4 each),
+//      then 16 score products over 2 accumulators (8 each, the first from C = 0);
+//   2: as 1 with the scores over 4 accumulators (4 each, the first two from C = 0);
+//   3: as 1 with every A operand read from LDS four products ahead (1 KiB per wave and
+//      read, conflict free).
+constexpr int kOrderLdsWords = 96 * 256;  // 96 KiB
+
+__device__ __forceinline__ f32x16 mfma32_pinned(const u32x4& a, const u32x4& b, const f32x16& c) {
+  const f32x16 d = mfma32(a, b, c);
+  __builtin_amdgcn_sched_barrier(0);
+  return d;
+}
+
+__global__ __launch_bounds__(kMicroThreads, 1) void mfma_order(unsigned long long* __restrict__ ticks,
+                                                             float* __restrict__ sink, int variant, int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t pad[kOrderLdsWords];
+  const int tid = threadIdx.x;
+  const u32x4 a = {0x3A803A80u, 0x3A803A80u, 0x3A803A80u, 0x3A803A80u};
+  u32x4 b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t x = 0x3A80u + (uint32_t)k;  // bf16 2^-10 (1 + k/128)
+    b[k] = u32x4{x | (x << 16), x | (x << 16), x | (x << 16), x | (x << 16)};
+  }
+  for (int e = tid; e < kOrderLdsWords; e += kMicroThreads) pad[e] = 0x3A803A80u;
+  __syncthreads();
+  f32x16 o[4], s[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = f32x16{};
+    s[k] = f32x16{};
+  }
+  float acc = 0.f;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  if (variant == 0) {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = mfma32_pinned(a, b[k], o[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s[k] = mfma32_pinned(a, b[4 + k], s[k]);
+      }
+    }
+  } else if (variant == 1) {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = mfma32_pinned(a, b[db], o[db]);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32_pinned(a, b[4 + kb], kk == 0 ? f32x16{} : s[kb]);
+      acc += s[0][0] + s[1][0];
+    }
+  } else if (variant == 2) {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = mfma32_pinned(a, b[db], o[db]);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int x = kb + 2 * (kk & 1);
+          s[x] = mfma32_pinned(a, b[4 + x], kk < 2 ? f32x16{} : s[x]);
+        }
+      acc += (s[0][0] + s[2][0]) + (s[1][0] + s[3][0]);
+    }
+  } else {
+    // byte offsets: 16 * lane + 8192 * wave + 1024 * (j % 8) + 16 <= 32768 < 98304
+    const unsigned char* base = (const unsigned char*)pad;
+    const uint32_t lb = 16u * (tid & 63) + 8192u * (tid >> 6);
+    for (int i = 0; i < iters; ++i) {
+      u32x4 fr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fr[j] = lds_read128(base, lb + 1024u * j);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const u32x4 av = fr[j & 3];
+        if (j + 4 < 32) fr[j & 3] = lds_read128(base, lb + 1024u * ((j + 4) & 7));
+        __builtin_amdgcn_sched_barrier(0);
+        if (j < 16) {
+          o[j & 3] = mfma32_pinned(av, b[j & 3], o[j & 3]);
+        } else {
+          const int kk = (j - 16) >> 1, kb = (j - 16) & 1;
+          s[kb] = mfma32_pinned(av, b[4 + kb], kk == 0 ? f32x16{} : s[kb]);
+        }
+      }
+      acc += s[0][0] + s[1][0];
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  float r = acc;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r += o[k][e] + s[k][e];
+  sink[(size_t)blockIdx.x * kMicroThreads + tid] = r;
+  if ((tid & 63) == 0) ticks[(size_t)blockIdx.x * 4 + (tid >> 6)] = t1 - t0;
+}
+
 int cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -250,6 +363,14 @@ int fa_micro_coexec(float* out, int blocks, int mode, int valu_kind, int mfma_it
     return -1;
   hipLaunchKernelGGL(fa355::coexec_loop, dim3(blocks), dim3(fa355::kCoexThreads), 0, (hipStream_t)stream, out, mode,
                      valu_kind, mfma_iters, valu_iters);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int fa_micro_mfma_order(unsigned long long* ticks, float* sink, int blocks, int variant, int iters,
+                        fa_stream_t stream) {
+  if (!ticks || !sink || blocks < 1 || variant < 0 || variant > 3 || iters < 1) return -1;
+  hipLaunchKernelGGL(fa355::mfma_order, dim3(blocks), dim3(fa355::kMicroThreads), 0, (hipStream_t)stream, ticks, sink,
+                     variant, iters);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

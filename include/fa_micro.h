@@ -68,6 +68,24 @@ int fa_micro_atomic_tiles(float* buf, int ntiles, int blocks, int tiles, fa_stre
 int fa_micro_coexec(float* out, int blocks, int mode, int valu_kind, int mfma_iters, int valu_iters,
                     fa_stream_t stream);
 
+/* Issue rate of bf16 products in a given order: one 256-thread workgroup per compute unit
+ * (96 KiB of LDS each), one wave per SIMD.  A operands are bf16 2^-10; accumulation
+ * chain k takes B = bf16 2^-10 (1 + k/128) (o[0..3]: k = 0..3, the score accumulators
+ * k = 4..), so each product adds 2^-16 (1 + k/128) to every element of its accumulator.
+ * Each wave runs `iters` blocks of 32 v_mfma_f32_32x32x16_bf16 and its lane 0 writes the
+ * s_memtime difference (shader-clock ticks) to ticks[block * 4 + wave]; 32 products take
+ * at least 32 * 32 = 1024 ticks.  variant 0: 8 independent chains (4 products each per
+ * block); 1: the attention forward's MFMA operation -- 16 P.V products over 4
+ * accumulators, then 16 score products over 2 accumulators, the first from C = 0;
+ * 2: as 1 with the scores over 4 accumulators (the first two from C = 0); 3: as 1 with
+ * every A operand read from LDS four products ahead.  sink[block * 256 + t] receives
+ * thread t's total: the per-block score sums (element 0 of each score accumulator) plus
+ * every accumulator element at the end (variants 1 and 3 compute the same values).
+ * ticks: blocks * 4 entries, sink: blocks * 256 floats, device pointers.  Returns -1 for
+ * a NULL pointer, blocks or iters below 1 or a variant outside 0..3. */
+int fa_micro_mfma_order(unsigned long long* ticks, float* sink, int blocks, int variant, int iters,
+                        fa_stream_t stream);
+
 /* Accumulation precision of the fp8 matrix product: one v_mfma_scale_f32_32x32x64_f8f6f4
  * (OCP E4M3 codes for both operands, unit scales) on one wave, C = A B^T + C0.  a and b
  * hold 32 x 64 E4M3 codes row-major (row i of b is column i of B), c0 and c 32 x 32

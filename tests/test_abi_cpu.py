@@ -235,7 +235,7 @@ def test_micro_library_exports_every_declared_symbol():
     with open(MICRO_HEADER) as f:
         names = sorted(set(re.findall(r"^\s*int\s+(fa_micro_\w+)\s*\(", f.read(), re.M)))
     assert names == ["fa_micro_atomic_tiles", "fa_micro_coexec", "fa_micro_exp", "fa_micro_grid_blocks",
-                     "fa_micro_lds_read", "fa_micro_mfma_bf16", "fa_micro_mfma_fp8_tile"]
+                     "fa_micro_lds_read", "fa_micro_mfma_bf16", "fa_micro_mfma_fp8_tile", "fa_micro_mfma_order"]
     lib = ctypes.CDLL(MICRO_LIB_PATH)
     for name in names:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr), name
@@ -253,6 +253,10 @@ def test_micro_library_exports_every_declared_symbol():
     for args in ((None, 1, 3, 0, 1, 1), (vp(16), 1, 0, 0, 1, 1), (vp(16), 1, 4, 0, 1, 1), (vp(16), 1, 3, 4, 1, 1), (vp(16), 1, 3, -1, 1, 1),
                  (vp(16), 1, 3, 0, 0, 1), (vp(16), 1, 3, 0, 1, 0), (vp(16), 0, 3, 0, 1, 1)):
         assert lib.fa_micro_coexec(*args, None) == -1, args
+    lib.fa_micro_mfma_order.argtypes = [vp, vp, i, i, i, vp]
+    for args in ((None, vp(16), 1, 0, 1), (vp(16), None, 1, 0, 1), (vp(16), vp(16), 0, 0, 1), (vp(16), vp(16), 1, -1, 1),
+                 (vp(16), vp(16), 1, 4, 1), (vp(16), vp(16), 1, 0, 0)):
+        assert lib.fa_micro_mfma_order(*args, None) == -1, args
     lib.fa_micro_mfma_fp8_tile.argtypes = [vp, vp, vp, vp, vp]
     for k in range(4):
         ptrs = [vp(16)] * 4

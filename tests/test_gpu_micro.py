@@ -219,3 +219,45 @@ def test_mfma_fp8_accumulation_precision(gpu, micro):
               f"mean signed err/|small| {np.mean((got - exact) / np.maximum(np.abs(small), 1e-30)):.3e}")
         assert np.all(np.isfinite(got))
         assert rel.max() <= 2.0**-10, name
+
+
+def test_mfma_order_sums_and_ticks(gpu, micro):
+    """The product-order probe: chain k's products add u_k = 2^-16 (1 + k/128) to each of
+    its accumulator elements, so each variant's per-thread total follows from its product
+    counts (exact in fp32 at 20 blocks); the forward's order with LDS operands computes
+    what it computes from registers; 32 products of 32 cycles each take at least 1024
+    shader-clock ticks per block, and no order beats independent chains."""
+    import torch
+
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    micro.fa_micro_mfma_order.argtypes = [vp, vp, i, i, i, vp]
+    micro.fa_micro_mfma_order.restype = i
+    blocks, iters = 4, 20
+    u = [2.0**-16 * (1 + k / 128) for k in range(8)]
+    pv = sum(16 * 4 * iters * u[k] for k in range(4))  # P.V accumulators at the end
+    expected = {
+        0: pv + sum(16 * 4 * iters * u[4 + k] for k in range(4)),
+        1: iters * (8 * u[4] + 8 * u[5]) + pv + 16 * 8 * (u[4] + u[5]),
+        2: iters * ((4 * u[4] + 4 * u[6]) + (4 * u[5] + 4 * u[7])) + pv + 16 * 4 * sum(u[4:8]),
+    }
+    expected[3] = expected[1]
+
+    def run(variant, n):
+        ticks = torch.zeros(blocks * 4, dtype=torch.int64, device=gpu)
+        sink = torch.full((blocks * 256,), -1.0, dtype=torch.float32, device=gpu)
+        assert micro.fa_micro_mfma_order(ticks.data_ptr(), sink.data_ptr(), blocks, variant, n, None) == 0
+        torch.cuda.synchronize()
+        return ticks.cpu().numpy() / n, sink.cpu().numpy()
+
+    per_block = {}
+    for variant in range(4):
+        P.say(f"micro mfma order variant {variant}")
+        t, sink = run(variant, iters)
+        np.testing.assert_array_equal(sink, np.float32(expected[variant]))
+        assert (t >= 0.97 * 1024).all(), (variant, t)
+        t, _ = run(variant, 400)
+        assert (t >= 0.97 * 1024).all(), (variant, t)
+        per_block[variant] = float(np.median(t))
+    P.say(f"  ticks per 32 products (400 blocks): {per_block}")
+    assert per_block[0] <= 1.25 * 1024
+    assert min(per_block[1], per_block[2], per_block[3]) >= 0.98 * per_block[0]
