@@ -348,9 +348,10 @@ def run_gpu(args):
     kind, causal = dom
     dom_flops = KERNEL_FLOP_SHARE[kind] * fwd_flops(B, H, N, d, causal)
     achieved = dom_flops / (kms[dom] * 1e-3) / 1e12
-    # template arguments: head dim, tile, causal, key padding (and, dK/dV pass, grouped K/V heads)
+    # template arguments: head dim, tile, causal, key padding, then the form the step's
+    # launches take: forward unsplit, dQ pass one wave group, dK/dV pass ungrouped heads
     kname = f"{KERNEL_NAME[kind]}<{d}, {64 if d == 128 else 128}, {'true' if causal else 'false'}, false" + (
-        ", false>" if kind == "dkdv" else ">")
+        {"fwd": ", false>", "dq": ", 1>", "dkdv": ", false>"}[kind])
     roofline = {
         "bound": "mfma",
         "achieved": round(achieved, 1),

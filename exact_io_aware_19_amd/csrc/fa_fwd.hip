@@ -103,22 +103,31 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], float sl, f
   l_run += lt;
 }
 
-template <int D, int BN, bool CAUSAL, bool KVLEN>
+// SPLIT (small d = 128 grids): 128 query rows per workgroup; both wave groups own the
+// same rows (wave w: rows 32 * (w % 4) ..) and group g streams the g-th half of the key
+// tiles through LDS rings of its own, one phase apart as above; at the end the second
+// group's (m, l, O) is merged into the first's through LDS.  The schedule, the barriers
+// and the per-tile work of each wave are those of the unsplit kernel.
+template <int D, int BN, bool CAUSAL, bool KVLEN, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int TILE_BYTES = BN * D * 2;  // one K tile or one V^T tile
   constexpr int NKB = BN / 32;            // 32-key blocks per tile
   constexpr int NDB = D / 32;             // 32-row blocks of the head dim
   constexpr int NKK = D / 16;             // k-steps of the QK^T contraction
-  // LDS: 2-deep rings of K tiles (natural) at [0, 2*TILE_BYTES) and of V^T tiles at
-  // [2*TILE_BYTES, 4*TILE_BYTES)
-  auto kbuf = [&](int i) { return smem + i * TILE_BYTES; };
-  auto vbuf = [&](int i) { return smem + (2 + i) * TILE_BYTES; };
-
+  constexpr int BM = SPLIT ? kBM / 2 : kBM;  // query rows per workgroup
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
+  const int grp = w >> 2, wg = w & 3;  // wave group (one wave per SIMD) and wave in it
+  const int wr = SPLIT ? wg : w;        // this wave's 32-row slice of the block
+  // LDS: 2-deep rings of K tiles (natural) at [0, 2*TILE_BYTES) and of V^T tiles at
+  // [2*TILE_BYTES, 4*TILE_BYTES) (SPLIT: a ring pair per wave group)
+  unsigned char* const gsm = SPLIT ? smem + (size_t)grp * kLdsTiles * TILE_BYTES : smem;
+  auto kbuf = [&](int i) { return gsm + i * TILE_BYTES; };
+  auto vbuf = [&](int i) { return gsm + (2 + i) * TILE_BYTES; };
+
   const int BH = p.B * p.H;
-  const int nqb = (p.N + kBM - 1) / kBM;
+  const int nqb = (p.N + BM - 1) / BM;
   // no mask: each XCD works through whole heads; causal: heaviest query blocks first
   int blk, bh;
   block_order<!CAUSAL>((int)blockIdx.x, nqb, BH, blk, bh);
@@ -134,19 +143,23 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
 
   int kv_end = Nk;
   if constexpr (KVLEN) kv_end = min(max(p.kv_len[b], 0), Nk);
-  const int q0 = qbi * kBM;
-  const int qrow = q0 + w * kRowsPerWave + c;  // this lane's query row
+  const int q0 = qbi * BM;
+  const int qrow = q0 + wr * kRowsPerWave + c;  // this lane's query row
   // causal positions: query row i sits at key position q_off + i
   const int cq0 = q0 + p.q_off, cqrow = qrow + p.q_off;
   int kend = kv_end;
-  if constexpr (CAUSAL) kend = min(kend, cq0 + kBM);
+  if constexpr (CAUSAL) kend = min(kend, cq0 + BM);
   const int ntiles = (kend + BN - 1) / BN;
   // keys past wave_kend are masked for every row of this wave (tile skipping)
   int wave_kend = kend;
-  if constexpr (CAUSAL) wave_kend = min(kend, cq0 + w * kRowsPerWave + kRowsPerWave);
+  if constexpr (CAUSAL) wave_kend = min(kend, cq0 + wr * kRowsPerWave + kRowsPerWave);
+  // this group's tiles [jb, je); both groups run `nt` tile steps (SPLIT: the second
+  // group's last one is empty when the count is odd)
+  const int nt = SPLIT ? (ntiles + 1) / 2 : ntiles;
+  const int jb = SPLIT ? grp * nt : 0, je = SPLIT ? min(ntiles, jb + nt) : ntiles;
 
   if (ntiles == 0) {  // no admissible key for any row of this block (kv_len == 0)
-    if (qrow < N) {
+    if ((!SPLIT || grp == 0) && qrow < N) {
       f32x16 zero[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) zero[db] = f32x16{};
@@ -175,9 +188,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   float l_run = 0.f;        // this lane's partial row sum (the other half-wave holds the rest)
   const float sl = p.scale_log2;
 
-  const int grp = w >> 2, wg = w & 3;  // wave group (one wave per SIMD) and wave in it
-  VtHalf<BN, D> vh;
-  vh.init(tid & 255, grp);
+  // V^T: each group transposes half of every tile (SPLIT: each group all of its own)
+  constexpr int NVH = SPLIT ? 2 : 1;
+  VtHalf<BN, D> vh[NVH];
+#pragma unroll
+  for (int x = 0; x < NVH; ++x) vh[x].init(tid & 255, SPLIT ? x : grp);
+  auto v_fetch = [&](int row0) {
+#pragma unroll
+    for (int x = 0; x < NVH; ++x) vh[x].fetch(vg, row0, kv_end);
+  };
+  auto v_store = [&](unsigned char* tile, int k) {  // k < 4 * NVH
+    vh[k / 4].store(tile, k % 4);
+  };
   // one wave-instruction of the K tile copy by wave group 0 (4 per wave)
   constexpr int KCOPY = BN * (D / 8) / (4 * 64);
   auto k_copy = [&](int row0, unsigned char* tile, int ii) {
@@ -244,13 +266,13 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   // The V^T stores are unconditional, so the stream has no branches: operation -1 stores
   // V_0 (fetched before the loop), and the store of the last operation rewrites a
   // buffer no later phase reads.  The K copy is chosen per stream at compile time.
-  auto op_mfma = [&](int j) {  // j = -1: scores of tile 0 only
-    const bool do_pv = j >= 0 && j < ntiles && j * BN < wave_kend;
+  auto op_mfma = [&](int j) {  // j = -1: scores of the group's first tile only
+    const bool do_pv = j >= 0 && jb + j < je && (jb + j) * BN < wave_kend;
     const int jn = j + 1;
-    const bool do_s = jn < ntiles && jn * BN < wave_kend;
+    const bool do_s = jb + jn < je && (jb + jn) * BN < wave_kend;
     unsigned char* vnext = vbuf(jn & 1);
     unsigned char* knext = kbuf(j & 1);
-    const int krow = (j + 2) * BN;
+    const int krow = (jb + j + 2) * BN;
     const unsigned char* vb_ = vbuf(j & 1);
     const unsigned char* kt = kbuf(jn & 1);
     auto run = [&](auto cpk) {
@@ -258,9 +280,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
       auto side = [&](auto ic, auto mc) {
         constexpr int i = decltype(ic)::value, SP = decltype(mc)::value / 16;
         // placement (measured): the V^T column stores late in a full stream (products
-        // 24, 26, 28, 30 of 32), the K copies one every four products from 2
-        constexpr int V0 = SP == 2 ? 24 : 1, K0 = 2;
-        if constexpr (i >= V0 && (i - V0) % 2 == 0 && (i - V0) / 2 < 4) vh.store(vnext, (i - V0) / 2);
+        // 24, 26, 28, 30 of 32; SPLIT: 8 stores from 16), the K copies one every four
+        // products from 2
+        constexpr int NVS = 4 * NVH;
+        constexpr int V0 = SP == 2 ? 32 - 2 * NVS : 1, K0 = 2;
+        if constexpr (i >= V0 && (i - V0) % 2 == 0 && (i - V0) / 2 < NVS) v_store(vnext, (i - V0) / 2);
         if constexpr (CPK && i >= K0 && (i - K0) % 4 == 0 && (i - K0) / 4 < KCOPY) k_copy(krow, knext, (i - K0) / 4);
       };
       if (do_pv && do_s) mfma_stream(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV + NS>{}, vb_, kt, side);
@@ -268,23 +292,24 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
       else if (do_s) mfma_stream(std::integral_constant<int, NPV>{}, std::integral_constant<int, NS>{}, vb_, kt, side);
       else {
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) vh.store(vnext, c4);
+        for (int c4 = 0; c4 < 4 * NVH; ++c4) v_store(vnext, c4);
         if constexpr (CPK) {
 #pragma unroll
           for (int ii = 0; ii < KCOPY; ++ii) k_copy(krow, knext, ii);
         }
       }
     };
-    if (grp == 0 && j + 2 < ntiles) run(std::true_type{});
+    // K_{j+2}: wave group 0 copies it for both groups (SPLIT: each group its own)
+    if ((SPLIT || grp == 0) && jb + j + 2 < je) run(std::true_type{});
     else run(std::false_type{});
   };
 
   // VALU operation for tile j: mask, online softmax with conditional rescaling, P -> pk.
   auto op_softmax = [&](int j) {
-    const int kt0 = j * BN;
-    if (j >= ntiles || kt0 >= wave_kend) return;
+    const int kt0 = (jb + j) * BN;
+    if (jb + j >= je || kt0 >= wave_kend) return;
     bool need_mask = kt0 + BN > kv_end;
-    if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > cq0 + w * kRowsPerWave);
+    if constexpr (CAUSAL) need_mask = need_mask || (kt0 + BN - 1 > cq0 + wr * kRowsPerWave);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -313,25 +338,57 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
   // Both land before the barrier that ends phase 2j+3, in buffers whose previous
   // contents (V_{j-1}, K_j) were last read in phase 2j+1, so both rings are two deep.
   // V_0 is fetched here and written by MFMA operation -1 (phases 0 and 1).
-  load_nat_tile<BN, D, kWaves>(kg, 0, kv_end, kbuf(0), w, l);
-  vh.fetch(vg, 0, kv_end);
+  if constexpr (SPLIT) {
+    if (jb < je) {
+      load_nat_tile<BN, D, 4>(kg, jb * BN, kv_end, kbuf(0), wg, l);
+      v_fetch(jb * BN);
+    }
+  } else {
+    load_nat_tile<BN, D, kWaves>(kg, 0, kv_end, kbuf(0), w, l);
+    v_fetch(0);
+  }
   wait_vmem();
   __syncthreads();
   // operation index of group 0 in phase ph is ph, of group 1 is ph - 1:
   //   op 0 = S_0, op 2j+1 = softmax_j, op 2j+2 = (PV_j, S_{j+1})
-  for (int ph = 0; ph < 2 * ntiles + 2; ++ph) {
+  for (int ph = 0; ph < 2 * nt + 2; ++ph) {
     const int op = ph - grp;
     if (op >= 0) {
       if (op & 1) {
         const int j = op >> 1;
-        if (j + 1 < ntiles) vh.fetch(vg, (j + 1) * BN, kv_end);
+        if (jb + j + 1 < je) v_fetch((jb + j + 1) * BN);
         op_softmax(j);
-        if (grp == 0) wait_vmem();
+        if (SPLIT || grp == 0) wait_vmem();
       } else {
         op_mfma((op >> 1) - 1);
       }
     }
     lds_barrier();
+  }
+  if constexpr (SPLIT) {
+    // merge: group 1 leaves (m, l, O) of each lane in LDS (the tiles are free after the
+    // loop's last barrier); group 0 rescales both to the larger reference
+    float* xo = (float*)smem + (size_t)(wg * 64 + l) * (16 * NDB + 2);
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[16 * db + r] = o[db][r];
+      xo[16 * NDB] = m_run;
+      xo[16 * NDB + 1] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xo[16 * NDB], l1 = xo[16 * NDB + 1];
+    const float mm = fmaxf(m_run, m1);
+    const float mr = (mm == -INFINITY) ? 0.f : mm;
+    const float a0 = fast_exp2(m_run - mr), a1 = fast_exp2(m1 - mr);
+    m_run = mm;
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[16 * db + r] * a1;
   }
 
   // ---- epilogue: normalise once, store O and LSE
@@ -347,36 +404,26 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs p) {
 // ---------------------------------------------------------------------------------
 // Small-grid forward: 4 waves (one per SIMD) = 128 query rows per workgroup, two
 // workgroups per CU, a straight tile loop (copy tile j+1 | S_j, softmax, P V_j | store
-// V_{j+1}^T | barrier).  With G = 1 each wave computes exactly what it computes in the
+// V_{j+1}^T | barrier).  Each wave computes exactly what it computes in the unsplit
 // kernel above (same rows, tiles, order and arithmetic: outputs equal bit for bit,
-// tested); the
-// smaller workgroups fill the GPU better where the 8-wave grid is small.  Measured on one
+// tested); the smaller workgroups fill the GPU better where the 8-wave grid is small.  Measured on one
 // box (ms, 8-wave -> this kernel): BERT-shaped (8,16,512,64, padded) 0.0173 -> 0.0158,
 // GPT-2-shaped causal (8,12,1024,64) 0.0331 -> 0.0288, (1,2,128,64) 0.0070 -> 0.0053;
 // slower on large grids (d=128, N=8192: 1.06 -> 1.18; d=64, N=65536 causal: 9.86 ->
 // 10.44) and at d=128, N=2048 (0.0725 -> 0.0815).
 // ---------------------------------------------------------------------------------
-constexpr int kW2 = 4;                    // waves per wave group (one per SIMD)
+constexpr int kW2 = 4;                    // waves per workgroup (one per SIMD)
 constexpr int kBM2 = kW2 * kRowsPerWave;  // query rows per workgroup
-// G = 1: one wave group, the whole key range.  G = 2 (split): two wave groups (8 waves,
-// two per SIMD) on the same 128 query rows, group g taking the g-th half of the key
-// tiles through LDS tiles of its own; the halves' (max, sum, O) are merged through LDS
-// at the end (so its sums differ from the unsplit kernels' in rounding only).  The split
-// halves every workgroup's tile count, so small grids (and the uneven blocks of a causal
-// mask) spread over twice as many SIMD slots.
-template <int D, int BN, bool CAUSAL, bool KVLEN, int G>
-__global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdArgs p) {
+template <int D, int BN, bool CAUSAL, bool KVLEN>
+__global__ __launch_bounds__(kW2 * 64, 2) void fa_fwd_small_kernel(FwdArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   constexpr int TILE_BYTES = BN * D * 2;
   constexpr int NKB = BN / 32, NDB = D / 32, NKK = D / 16;
 
   const int tid = threadIdx.x;
-  const int wg = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
-  const int grp = G == 1 ? 0 : (wg >> 2), w = G == 1 ? wg : (wg & 3);
-  const int gtid = G == 1 ? tid : (tid & 255);
-  unsigned char* const gsm = smem + (size_t)grp * kLdsTiles * TILE_BYTES;
-  auto kbuf = [&](int i) { return gsm + i * TILE_BYTES; };
-  auto vbuf = [&](int i) { return gsm + (2 + i) * TILE_BYTES; };
+  const int w = tid >> 6, l = tid & 63, c = l & 31, h = l >> 5;
+  auto kbuf = [&](int i) { return smem + i * TILE_BYTES; };
+  auto vbuf = [&](int i) { return smem + (2 + i) * TILE_BYTES; };
   const int BH = p.B * p.H;
   const int nqb = (p.N + kBM2 - 1) / kBM2;
   int blk, bh;
@@ -402,7 +449,7 @@ __global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdAr
   if constexpr (CAUSAL) wave_kend = min(kend, cq0 + w * kRowsPerWave + kRowsPerWave);
 
   if (ntiles == 0) {
-    if ((G == 1 || grp == 0) && qrow < N) {
+    if (qrow < N) {
       f32x16 zero[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) zero[db] = f32x16{};
@@ -431,37 +478,31 @@ __global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdAr
   const float sl = p.scale_log2;
 
   VtHalf<BN, D> vh[2];
-  vh[0].init(gtid, 0);
-  vh[1].init(gtid, 1);
+  vh[0].init(tid, 0);
+  vh[1].init(tid, 1);
   const uint32_t kfrag = NatFrag<D>::base(c, h);
   const uint32_t vfrag[2] = {TrFrag<BN>::base(c, h, 0), TrFrag<BN>::base(c, h, 1)};
 
-  // this group's tiles [jb, je); with G = 2 both groups run the first group's count of
-  // iterations (the second group's last one is empty when the count is odd)
-  const int half = G == 1 ? ntiles : (ntiles + 1) / 2;
-  const int jb = G == 1 ? 0 : grp * half, je = G == 1 ? ntiles : min(ntiles, jb + half);
-  if (G == 1 || jb < je) {
-    load_nat_tile<BN, D, kW2>(kg, jb * BN, kv_end, kbuf(0), w, l);
-    vh[0].fetch(vg, jb * BN, kv_end);
-    vh[1].fetch(vg, jb * BN, kv_end);
+  load_nat_tile<BN, D, kW2>(kg, 0, kv_end, kbuf(0), w, l);
+  vh[0].fetch(vg, 0, kv_end);
+  vh[1].fetch(vg, 0, kv_end);
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      vh[0].store(vbuf(0), c4);
-      vh[1].store(vbuf(0), c4);
-    }
+  for (int c4 = 0; c4 < 4; ++c4) {
+    vh[0].store(vbuf(0), c4);
+    vh[1].store(vbuf(0), c4);
   }
   wait_vmem();
   __syncthreads();
-  for (int j = jb; j < jb + half; ++j) {
-    const bool nxt = j + 1 < je;
+  for (int j = 0; j < ntiles; ++j) {
+    const bool nxt = j + 1 < ntiles;
     if (nxt) {
-      load_nat_tile<BN, D, kW2>(kg, (j + 1) * BN, kv_end, kbuf((j + 1 - jb) & 1), w, l);
+      load_nat_tile<BN, D, kW2>(kg, (j + 1) * BN, kv_end, kbuf((j + 1) & 1), w, l);
       vh[0].fetch(vg, (j + 1) * BN, kv_end);
       vh[1].fetch(vg, (j + 1) * BN, kv_end);
     }
     const int kt0 = j * BN;
-    if ((G == 1 || j < je) && kt0 < wave_kend) {
-      const unsigned char* kt = kbuf((j - jb) & 1);
+    if (kt0 < wave_kend) {
+      const unsigned char* kt = kbuf(j & 1);
       f32x16 s[NKB];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
@@ -489,7 +530,7 @@ __global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdAr
       }
       u32x4 pk[NKB][2];
       softmax_tile<false, NKB, NDB>(s, sl, m_run, l_run, o, pk);
-      const unsigned char* vb_ = vbuf((j - jb) & 1);
+      const unsigned char* vb_ = vbuf(j & 1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -503,39 +544,14 @@ __global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdAr
     if (nxt) {
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        vh[0].store(vbuf((j + 1 - jb) & 1), c4);
-        vh[1].store(vbuf((j + 1 - jb) & 1), c4);
+        vh[0].store(vbuf((j + 1) & 1), c4);
+        vh[1].store(vbuf((j + 1) & 1), c4);
       }
     }
     wait_vmem();
     __syncthreads();
   }
 
-  if constexpr (G == 2) {
-    // merge: group 1 leaves (m, l, O) of each lane in LDS (the tiles are free after the
-    // loop's last barrier); group 0 rescales both halves to the larger reference
-    float* xo = (float*)smem + (size_t)(w * 64 + l) * (16 * NDB + 2);
-    if (grp == 1) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xo[16 * db + r] = o[db][r];
-      xo[16 * NDB] = m_run;
-      xo[16 * NDB + 1] = l_run;
-    }
-    __syncthreads();
-    if (grp == 1) return;
-    const float m1 = xo[16 * NDB], l1 = xo[16 * NDB + 1];
-    const float mm = fmaxf(m_run, m1);
-    const float mr = (mm == -INFINITY) ? 0.f : mm;
-    const float a0 = fast_exp2(m_run - mr), a1 = fast_exp2(m1 - mr);
-    m_run = mm;
-    l_run = l_run * a0 + l1 * a1;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[16 * db + r] * a1;
-  }
   const float l_tot = half_sum(l_run);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
@@ -547,9 +563,13 @@ __global__ __launch_bounds__(kW2 * 64 * G, 3 - G) void fa_fwd_small_kernel(FwdAr
 
 // Grids of the 8-wave kernel below this many workgroups (two per CU) run the small-grid
 // kernel when d = 64 (where it measured faster; at d = 128 it did not).  At d = 128 the
-// smallest grids run its split form instead (split_small_grid: B=1, H=16, N=2048 causal
-// 0.0598 -> 0.0476 ms, no mask 0.0624 -> 0.0519; B=2, H=16, N=2048 causal 0.0660 ->
-// 0.0628; one box), which measured slower at d = 64 and on fuller grids.
+// smallest grids (split_small_grid) run the 8-wave kernel's split form instead, 128 rows
+// per workgroup with each wave group on half of the key tiles.  Measured (ms): a split on
+// the 4-wave straight loop with the groups in lockstep against the unsplit kernel (one
+// box): B=1, H=16, N=2048 causal 0.0598 -> 0.0476, no mask 0.0624 -> 0.0519; B=2, H=16,
+// N=2048 causal 0.0660 -> 0.0628; this ping-pong split against that lockstep split
+// (another box): 0.0473 -> 0.0433, 0.0538 -> 0.0496, 0.0643 -> 0.0601, and B=2, H=16,
+// N=1024 causal 0.0293 -> 0.0281.  Splits measured slower at d = 64 and on fuller grids.
 constexpr unsigned kSmallGrid = 512;
 
 template <int D, int BN, bool CAUSAL, bool KVLEN>
@@ -559,17 +579,17 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   const unsigned grid8 = (unsigned)((a.N + kBM - 1) / kBM) * bh;
   if constexpr (D == 128) {
     if (split_small_grid(grid8, CAUSAL)) {
-      auto kern = fa_fwd_small_kernel<D, BN, CAUSAL, KVLEN, 2>;
+      auto kern = fa_fwd_kernel<D, BN, CAUSAL, KVLEN, true>;
       const size_t lds2 = 2 * lds;
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
       if (e != hipSuccess) return e;
-      const unsigned grid = (unsigned)((a.N + kBM2 - 1) / kBM2) * bh;
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * kW2 * 64), lds2, stream, a);
+      const unsigned grid = (unsigned)((a.N + kBM / 2 - 1) / (kBM / 2)) * bh;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds2, stream, a);
       return hipGetLastError();
     }
   }
   if (D == 64 && grid8 < kSmallGrid) {
-    auto kern = fa_fwd_small_kernel<D, BN, CAUSAL, KVLEN, 1>;
+    auto kern = fa_fwd_small_kernel<D, BN, CAUSAL, KVLEN>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((a.N + kBM2 - 1) / kBM2) * bh;
