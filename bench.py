@@ -370,22 +370,27 @@ def run_gpu(args):
     sweep = []
     if args.sweep:
         sweep = run_sweep(fa, wl, torch, dev, stream)
-    # the calibration copies come last: the counter summary takes the last ten copy
-    # dispatches of the run
-    if args.copy_calibration:
-        nbytes = COPY_CAL_MIB << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            dst.copy_(src)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        roofline["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(e0.elapsed_time(e1) / 10, 4)}
     return value, wall, detail, roofline, (B, H, N, d), inp, sweep
+
+
+def copy_calibration(torch):
+    """Ten plain device copies of COPY_CAL_MIB MiB (plus one untimed) whose FETCH_SIZE and
+    WRITE_SIZE readings calibrate the counters.  main() runs them as the last GPU work of
+    the run: the counter summary takes the last ten copy dispatches."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    nbytes = COPY_CAL_MIB << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(e0.elapsed_time(e1) / 10, 4)}
 
 
 def run_fp8(fa, wl, torch, dev, stream, t, w, iters):
@@ -906,7 +911,7 @@ def summarize_pmc(fetch_csv, write_csv, out_md, by_grid=False):
         "",
         "    rocprofv3 --pmc FETCH_SIZE -f csv -d %s -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration%s" % (fdir, sweep),
         "    rocprofv3 --pmc WRITE_SIZE -f csv -d %s -o p -- python bench.py --steps 2 --warmup 1 --cpu-heads 0 --copy-calibration%s" % (wdir, sweep),
-        "    python bench.py --summarize-pmc%s %s %s %s"
+        "    python bench.py%s --summarize-pmc %s %s %s"
         % (" --pmc-by-grid" if by_grid else "", os.path.relpath(os.path.abspath(fetch_csv), ROOT),
            os.path.relpath(os.path.abspath(write_csv), ROOT), os.path.relpath(out_md, ROOT)),
         "",
@@ -982,6 +987,10 @@ def main(argv=None):
         detail["machine"] = m = run_machine(torch, torch.device("cuda:0"), torch.cuda.current_stream())
         # the dominant kernel against the MFMA rate the chip sustains, beside the data-sheet peak
         roofline["frac_of_sustained_mfma"] = round(roofline["achieved"] / m["mfma_bf16_tflops"], 4)
+    if args.copy_calibration:  # last: no copy may follow the calibration copies
+        import torch
+
+        roofline["copy_calibration"] = copy_calibration(torch)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
